@@ -1,0 +1,180 @@
+/*
+ * moe.h -- C ABI of libmoe: the Nemotron-H MoE layer forward on MI355X (gfx950).
+ *
+ * The layer (baseRT issue "Requesting converter + runtime support for the
+ * Nemotron-H architecture", section "Architecture (config.json)"; exo commit
+ * "Add support for Nemotron sharding", typing stub of NemotronHMoE /
+ * SwitchMLP / NemotronHMLP):
+ *
+ *   l = x Wg^T;  s = sigmoid(l);  c = s + e_bias       (bias selects only)
+ *   groups: gs_g = sum of the two largest c in group g; keep topk_group groups,
+ *           then the top_k experts of largest c inside them (ties: lower index)
+ *   w_j = routed_scaling_factor * s_j / sum s    (norm_topk_prob; else scale * s_j)
+ *   y = sum_j w_j Wdown[e_j] relu(Wup[e_j] x)^2  +  Ws_down relu(Ws_up x)^2
+ *
+ * Experts are non-gated up_proj -> relu^2 -> down_proj (vllm.cpp PR
+ * "spec(MODEL-TEXT-nemotron-h)"), without biases (auto-round PR "feat:
+ * support Nemotron-H / Nemotron-Cascade-2", quantisation log).
+ *
+ * Conventions shared by every entry point
+ *  - Array arguments are DEVICE pointers unless marked (host); arrays are
+ *    row-major and contiguous; every array pointer must be 16-byte aligned.
+ *    bf16 arrays hold IEEE bfloat16 bit patterns; fp8 arrays hold OCP e4m3fn
+ *    codes.
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates or frees memory, never synchronises, and keeps no state between
+ *    calls; all work is enqueued on `stream` (a hipStream_t, NULL = the null
+ *    stream) and the call returns at once.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED /
+ *    MOE_ERR_WORKSPACE and enqueues nothing.  A failed launch returns
+ *    MOE_ERR_HIP.  Faults during execution surface at the caller's next
+ *    synchronisation.
+ *  - tokens == 0 is valid: nothing is enqueued and MOE_OK is returned.
+ *  - Calls on one stream with one workspace run in order; concurrent calls
+ *    need distinct workspaces.
+ *  - Inputs must be finite; routing of NaN/Inf scores is unspecified.
+ *  - Results are deterministic: no floating-point atomics, fixed reduction
+ *    orders, so reruns are bitwise identical.
+ */
+#ifndef NGR_MOE_H
+#define NGR_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, misalignment, inconsistent sizes   */
+  MOE_ERR_UNSUPPORTED = 2, /* valid layer, but outside what the kernels cover  */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required       */
+  MOE_ERR_HIP = 4          /* a HIP launch failed                              */
+} moe_status;
+
+typedef enum moe_dtype {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2 /* routed expert weights only, with fp32 per-row scales */
+} moe_dtype;
+
+/* Layer configuration; names follow the model config (exo commit "Add support
+ * for Nemotron sharding", ModelArgs).  n_group is the ROUTING group count
+ * (the config field n_group), not the Mamba n_groups. */
+typedef struct moe_config {
+  int32_t hidden;        /* d  (hidden_size), multiple of 64                        */
+  int32_t n_experts;     /* E  (n_routed_experts), multiple of 16, <= 256            */
+  int32_t n_group;       /* G  routing groups, divides E, <= 64                      */
+  int32_t topk_group;    /* tg groups kept per token, 1..G                           */
+  int32_t top_k;         /* k  (num_experts_per_tok), 1..min(tg*E/G, 32)             */
+  int32_t inter;         /* I  (moe_intermediate_size), multiple of 64               */
+  int32_t shared_inter;  /* Is (moe_shared_expert_intermediate_size), multiple of 64;
+                            0 = no shared expert                                     */
+  int32_t norm_topk_prob;/* 0 or 1                                                   */
+  float routed_scaling_factor;
+  int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, w_gate, shared weights, y        */
+  int32_t expert_dtype;  /* routed weights: MOE_F32 (needs act F32), MOE_BF16 or
+                            MOE_FP8_E4M3 (both need act BF16)                        */
+} moe_config;
+
+/* Bytes of workspace moe_forward needs for `tokens` tokens (host output). The
+ * same workspace also serves moe_route and moe_permute at that size. */
+moe_status moe_workspace_size(const moe_config* cfg, int64_t tokens, size_t* bytes);
+
+/* Router and grouped top-k selection (the first two lines of the layer above).
+ *   x        [tokens, d]  act_dtype
+ *   w_gate   [E, d]       act_dtype (the gate is never quantised: auto-round
+ *                         log, predefined ignore_layers ``mixer.gate``)
+ *   e_bias   [E]          fp32 correction bias, used only to select
+ *   topk_idx [tokens, k]  int32 out, each row ascending by expert id
+ *   topk_w   [tokens, k]  fp32 out, aligned with topk_idx
+ * Logits accumulate in fp32; scores, group sums and comparisons are fp32. */
+moe_status moe_route(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
+                     const float* e_bias, int32_t* topk_idx, float* topk_w, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Stable grouping of the tokens*k routing slots (slot s = t*k + j) by expert:
+ *   expert_counts  [E]        int32 out
+ *   expert_offsets [E+1]      int32 out, exclusive prefix sum of the counts
+ *   sorted_slot    [tokens*k] int32 out, slot at each sorted position; within
+ *                             one expert the slots ascend
+ *   slot_pos       [tokens*k] int32 out, inverse of sorted_slot
+ *   x, x_perm      optional (both NULL or both set): x_perm [tokens*k, d]
+ *                  act_dtype receives x[sorted_slot[p] / k] at row p
+ * topk_idx values must lie in [0, E). */
+moe_status moe_permute(const moe_config* cfg, int64_t tokens, const int32_t* topk_idx,
+                       int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_slot,
+                       int32_t* slot_pos, const void* x, void* x_perm, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_expert_ffn needs for one call (host output). */
+moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, int32_t inter,
+                                         int32_t w_dtype, int64_t a_rows, int64_t rows,
+                                         size_t* bytes);
+
+/* Grouped non-gated expert MLPs: for each matrix pair m and each problem row r
+ * in [row_offsets[m], row_offsets[m+1]):
+ *     out[r] = Wdown[m] relu(Wup[m] a[src(r)])^2,  src(r) = row_index[r] / index_div
+ *                                                  (or r when row_index is NULL)
+ *   a            [a_rows, d] act_dtype
+ *   row_offsets  [n_mats+1] int32, ascending, row_offsets[0] = 0,
+ *                row_offsets[n_mats] = rows (values are clamped to [0, rows])
+ *   row_index    [rows] int32 or NULL; index_div >= 1; sources clamp to a_rows-1
+ *   w_up         [n_mats, inter, d], w_down [n_mats, d, inter], of w_dtype
+ *   w_up_scale   [n_mats, inter], w_down_scale [n_mats, d]: fp32 per-row scales
+ *                for MOE_FP8_E4M3 weights, else NULL
+ *   out          [rows, d] fp32
+ * With fp8 weights each a row is quantised per row to e4m3 (scale amax/448,
+ * nearest even, saturating) before the up GEMM and each h row likewise before
+ * the down GEMM; both GEMMs run on fp8 MFMA with fp32 accumulation and the
+ * scales applied in the epilogue.  Otherwise h is rounded to the weights'
+ * type (bf16 nearest even, or fp32) and both GEMMs accumulate in fp32.
+ * The routed experts of the layer are the call (n_mats = E, a = x,
+ * row_offsets = expert_offsets, row_index = sorted_slot, index_div = k); the
+ * shared expert is (n_mats = 1, row_offsets = {0, tokens}, row_index = NULL). */
+moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, int32_t w_dtype,
+                          int64_t a_rows, const void* a, int64_t rows,
+                          const int32_t* row_offsets, const int32_t* row_index,
+                          int32_t index_div, const void* w_up, const float* w_up_scale,
+                          const void* w_down, const float* w_down_scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weighted combine (exo commit "Add support for Nemotron sharding": the shared
+ * expert's output joins the routed sum before the mixer's single reduction):
+ *     y[t] = sum_{j ascending} topk_w[t,j] * y_perm[slot_pos[t*k+j]] + shared_out[t]
+ * summed in fp32 and rounded once to act_dtype (nearest even for bf16).
+ *   slot_pos [tokens*k] int32, topk_w [tokens,k] fp32, y_perm [tokens*k, d] fp32,
+ *   shared_out [tokens, d] fp32 or NULL, y [tokens, d] act_dtype out. */
+moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slot_pos,
+                       const float* topk_w, const float* y_perm, const float* shared_out,
+                       void* y, void* stream);
+
+/* The whole layer: route -> permute -> routed expert MLPs -> shared expert ->
+ * combine, bit-identical to that composition of the entry points above.
+ *   x [tokens, d], w_gate [E, d], e_bias [E] fp32, w_up [E, I, d], w_down [E, d, I]
+ *   (expert_dtype; fp8 scales as in moe_expert_ffn), ws_up [Is, d], ws_down [d, Is]
+ *   (act_dtype), y [tokens, d] act_dtype out.
+ *   topk_idx [tokens,k], topk_w [tokens,k], expert_counts [E]: optional outputs
+ *   (NULL = not wanted).
+ *   workspace: at least moe_workspace_size(cfg, tokens) bytes. */
+moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
+                       const float* e_bias, const void* w_up, const float* w_up_scale,
+                       const void* w_down, const float* w_down_scale, const void* ws_up,
+                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status status);
+
+/* Version of this ABI (bumped on any signature or semantic change). */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGR_MOE_H */

@@ -1,0 +1,247 @@
+"""Thin ctypes binding of libmoe (include/moe.h) over torch device tensors.
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe.so; torch provides device memory and the current stream.  There is no
+fallback: without the built library every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("routed_scaling_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
+                ("expert_dtype", ctypes.c_int32)]
+
+
+def config_from(wl) -> MoeConfig:
+    """MoeConfig from any object with the workload fields (hidden, n_experts, ...)."""
+    return MoeConfig(wl.hidden, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k, wl.inter,
+                     wl.shared_inter, int(bool(wl.norm_topk_prob)),
+                     float(wl.routed_scaling_factor), DTYPE_CODE[wl.act_dtype],
+                     DTYPE_CODE[wl.expert_dtype])
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_cfgp = ctypes.POINTER(MoeConfig)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (torch is imported first so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(python -m non_gated_relu_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_abi_version.restype = ctypes.c_int32
+        L.moe_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_route.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_permute.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  ctypes.c_size_t, _vp]
+        L.moe_expert_ffn_workspace_size.argtypes = [_cfgp, _i32, _i32, _i32, _i64, _i64,
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_expert_ffn.argtypes = [_cfgp, _i32, _i32, _i32, _i64, _vp, _i64, _vp, _vp, _i32,
+                                     _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_combine.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.moe_forward.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        for name in ("moe_workspace_size", "moe_route", "moe_permute",
+                     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
+                     "moe_forward"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().moe_status_string(status).decode()} ({status})")
+
+
+class MoeValueError(MoeError, ValueError):
+    """Invalid or unsupported arguments (nothing was enqueued)."""
+
+
+def _check(status: int, where: str) -> None:
+    if status == MOE_OK:
+        return
+    if status in (MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE):
+        raise MoeValueError(status, where)
+    raise MoeError(status, where)
+
+
+def _p(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return _vp(t.data_ptr())
+
+
+def _stream():
+    return _vp(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t):
+    return t.device
+
+
+def _empty(shape, dtype, like):
+    return torch.empty(shape, dtype=dtype, device=like.device)
+
+
+def workspace_size(cfg: MoeConfig, tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg), tokens, ctypes.byref(n)),
+           "moe_workspace_size")
+    return n.value
+
+
+def expert_ffn_workspace_size(cfg: MoeConfig, n_mats: int, inter: int, w_dtype: int,
+                              a_rows: int, rows: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_expert_ffn_workspace_size(ctypes.byref(cfg), n_mats, inter, w_dtype, a_rows,
+                                               rows, ctypes.byref(n)),
+           "moe_expert_ffn_workspace_size")
+    return n.value
+
+
+def workspace(nbytes: int, like: torch.Tensor) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
+
+
+def route(cfg: MoeConfig, x, w_gate, e_bias, topk_idx=None, topk_w=None):
+    T = x.shape[0]
+    k = cfg.top_k
+    topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
+    topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(topk_idx),
+                           _p(topk_w), None, 0, _stream()), "moe_route")
+    return topk_idx, topk_w
+
+
+def permute(cfg: MoeConfig, topk_idx, x=None, with_x_perm: bool = False):
+    T = topk_idx.shape[0]
+    S = T * cfg.top_k
+    E = cfg.n_experts
+    counts = _empty((E,), torch.int32, topk_idx)
+    offsets = _empty((E + 1,), torch.int32, topk_idx)
+    sorted_slot = _empty((S,), torch.int32, topk_idx)
+    slot_pos = _empty((S,), torch.int32, topk_idx)
+    x_perm = None
+    if with_x_perm:
+        x_perm = _empty((S, x.shape[1]), x.dtype, x)
+    ws = workspace(workspace_size(cfg, T), topk_idx)
+    _check(lib().moe_permute(ctypes.byref(cfg), T, _p(topk_idx), _p(counts), _p(offsets),
+                             _p(sorted_slot), _p(slot_pos), _p(x) if with_x_perm else None,
+                             _p(x_perm), _p(ws), ws.numel(), _stream()), "moe_permute")
+    return dict(counts=counts, offsets=offsets, sorted_slot=sorted_slot, slot_pos=slot_pos,
+                x_perm=x_perm)
+
+
+def expert_ffn(cfg: MoeConfig, w_up, w_down, a, row_offsets, rows: int, row_index=None,
+               index_div: int = 1, w_dtype: str = None, w_up_scale=None, w_down_scale=None,
+               out=None):
+    """out[r] = Wdown[m] relu(Wup[m] a[src(r)])^2 over the grouped rows (see moe.h)."""
+    n_mats, inter = w_up.shape[0], w_up.shape[1]
+    w_dtype = w_dtype or {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}[
+        w_up.dtype]
+    code = DTYPE_CODE[w_dtype]
+    a_rows = a.shape[0]
+    out = _empty((rows, cfg.hidden), torch.float32, a) if out is None else out
+    ws = workspace(expert_ffn_workspace_size(cfg, n_mats, inter, code, a_rows, rows), a)
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg), n_mats, inter, code, a_rows, _p(a), rows,
+                                _p(row_offsets), _p(row_index), index_div, _p(w_up),
+                                _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(out), _p(ws),
+                                ws.numel(), _stream()), "moe_expert_ffn")
+    return out
+
+
+def combine(cfg: MoeConfig, slot_pos, topk_w, y_perm, shared_out=None, y=None):
+    T = topk_w.shape[0]
+    if y is None:
+        y = _empty((T, cfg.hidden), torch.bfloat16 if cfg.act_dtype == MOE_BF16 else torch.float32,
+                   y_perm)
+    _check(lib().moe_combine(ctypes.byref(cfg), T, _p(slot_pos), _p(topk_w), _p(y_perm),
+                             _p(shared_out), _p(y), _stream()), "moe_combine")
+    return y
+
+
+def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_up_scale=None,
+            w_down_scale=None, ws=None, y=None, topk_idx=None, topk_w=None, expert_counts=None):
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    if ws is None:
+        ws = workspace(workspace_size(cfg, T), x)
+    _check(lib().moe_forward(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(w_up),
+                             _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(ws_up),
+                             _p(ws_down), _p(y), _p(topk_idx), _p(topk_w), _p(expert_counts),
+                             _p(ws), ws.numel(), _stream()), "moe_forward")
+    return y
+
+
+class MoELayer:
+    """Device-resident weights of one MoE layer plus a reusable workspace.
+
+    ``layer(x)`` runs the whole forward through ``moe_forward``; the routing
+    of the last call is kept in ``topk_idx`` / ``topk_w`` / ``expert_counts``.
+    """
+
+    def __init__(self, wl, tensors: dict, device="cuda", max_tokens: int = None):
+        self.wl = wl
+        self.cfg = config_from(wl)
+        self.device = torch.device(device)
+        self.t = {k: to_device(v, device, k, wl) for k, v in tensors.items()
+                  if v is not None and k != "x"}
+        self.max_tokens = max_tokens or wl.tokens
+        self.ws = torch.empty(workspace_size(self.cfg, self.max_tokens), dtype=torch.uint8,
+                              device=self.device)
+        T, k = self.max_tokens, wl.top_k
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=self.device)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=self.device)
+        self.expert_counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=self.device)
+
+    def __call__(self, x, y=None):
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens exceed the workspace sized for {self.max_tokens}")
+        t = self.t
+        return forward(self.cfg, x, t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
+                       t.get("ws_up"), t.get("ws_down"), t.get("w_up_scale"),
+                       t.get("w_down_scale"), ws=self.ws, y=y, topk_idx=self.topk_idx[:T],
+                       topk_w=self.topk_w[:T], expert_counts=self.expert_counts)
+
+
+def to_device(a, device, name: str, wl):
+    """numpy storage array (fp32 / bf16 bits / fp8 codes) -> device tensor."""
+    import numpy as np
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to(device)

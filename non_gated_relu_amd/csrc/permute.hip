@@ -1,0 +1,305 @@
+// permute.hip -- stable grouping of routing slots by expert, tile schedules,
+// the optional row gather, and the weighted combine.
+//
+// The experts are applied as one stacked weight tensor per projection indexed
+// by the routing result (exo commit "Add support for Nemotron sharding",
+// typing stubs SwitchMLP.fc1 / fc2 and SwitchGLU.__call__(x, indices)); the
+// GEMMs want the rows of one expert contiguous, so slots s = t*k + j are
+// grouped by expert with a histogram, an exclusive scan and a stable
+// placement (slot ids ascend inside an expert).  No atomics decide an order:
+// LDS integer atomics only count, and ranks inside a wave come from ballots.
+#include "internal.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int PM_THREADS = 256;
+constexpr int PM_WAVES = PM_THREADS / WAVE;
+
+// Lanes of this wave holding the same key (keys < 2^9, one extra bit marks
+// validity), found with one ballot per key bit.
+__device__ __forceinline__ uint64_t match_key(uint32_t key) {
+  uint64_t m = ~uint64_t(0);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    uint64_t bb = ballot((key >> b) & 1u);
+    m &= ((key >> b) & 1u) ? bb : ~bb;
+  }
+  return m;
+}
+
+// Place the slots [s_begin, s_end) in order.  run[e] holds the next free
+// position of expert e and is advanced; wc is a zeroed [PM_WAVES][E] scratch.
+__device__ void place_chunk(const int32_t* __restrict__ idx, int64_t s_begin, int64_t s_end,
+                            int E, int32_t* run, int32_t* wc, int32_t* __restrict__ sorted_slot,
+                            int32_t* __restrict__ slot_pos) {
+  const int wave = threadIdx.x / WAVE;
+  const int lane = lane_id();
+  for (int64_t r0 = s_begin; r0 < s_end; r0 += PM_THREADS) {
+    const int64_t s = r0 + threadIdx.x;
+    const bool valid = s < s_end;
+    // ids outside [0, E) are clamped so that every write stays inside the arrays
+    const int e = valid ? min(max(idx[s], 0), E - 1) : 0;
+    const uint32_t key = valid ? (uint32_t(e) | 0x200u) : 0u;
+    const uint64_t m = match_key(key);
+    const int rank = __popcll(m & lanemask_lt());
+    if (valid && rank == 0) wc[wave * E + e] = __popcll(m);
+    __syncthreads();
+    int pos = 0;
+    if (valid) {
+      pos = run[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < E; x += PM_THREADS) {
+      int add = 0;
+      for (int w = 0; w < PM_WAVES; ++w) {
+        add += wc[w * E + x];
+        wc[w * E + x] = 0;
+      }
+      run[x] += add;
+    }
+    if (valid) {
+      sorted_slot[pos] = static_cast<int32_t>(s);
+      slot_pos[s] = pos;
+    }
+    __syncthreads();
+    (void)lane;
+  }
+}
+
+// Exclusive scan of n <= PM_THREADS * 4 values held in LDS `v` (in place);
+// returns the total.  All threads must call.
+__device__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* tmp) {
+  // each thread owns 4 consecutive entries
+  const int t = threadIdx.x;
+  int32_t loc[4];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int j = t * 4 + i;
+    loc[i] = j < n ? v[j] : 0;
+    sum += loc[i];
+  }
+  tmp[t] = sum;
+  __syncthreads();
+  // Hillis-Steele over PM_THREADS partial sums
+  for (int off = 1; off < PM_THREADS; off <<= 1) {
+    int32_t add = t >= off ? tmp[t - off] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  int32_t run = tmp[t] - sum;
+  const int32_t total = tmp[PM_THREADS - 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int j = t * 4 + i;
+    if (j < n) v[j] = run;
+    run += loc[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+// Small problems (all slots in one workgroup): histogram, scan, placement.
+__global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p) {
+  __shared__ int32_t cnt[1024];
+  __shared__ int32_t run[1024];
+  __shared__ int32_t wc[PM_WAVES * 256];
+  __shared__ int32_t tmp[PM_THREADS];
+  const int E = p.n_experts;
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
+  for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
+  __syncthreads();
+  for (int64_t s = threadIdx.x; s < p.slots; s += PM_THREADS) atomicAdd(&cnt[min(max(p.topk_idx[s], 0), E - 1)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+    run[e] = cnt[e];
+    p.expert_counts[e] = cnt[e];
+  }
+  __syncthreads();
+  block_exclusive_scan(run, E, tmp);
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) p.expert_offsets[e] = run[e];
+  if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
+  __syncthreads();
+  place_chunk(p.topk_idx, 0, p.slots, E, run, wc, p.sorted_slot, p.slot_pos);
+}
+
+// Large problems, pass 1: per-chunk expert histogram.
+__global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(PermuteArgs p) {
+  __shared__ int32_t cnt[256];
+  const int E = p.n_experts;
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
+  __syncthreads();
+  const int64_t s0 = int64_t(blockIdx.x) * p.chunk;
+  const int64_t s1 = min<int64_t>(s0 + p.chunk, p.slots);
+  for (int64_t s = s0 + threadIdx.x; s < s1; s += PM_THREADS) atomicAdd(&cnt[min(max(p.topk_idx[s], 0), E - 1)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) p.block_counts[blockIdx.x * E + e] = cnt[e];
+}
+
+// Pass 2 (one workgroup): per-expert totals, offsets, and each chunk's base.
+__global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p) {
+  __shared__ int32_t off[1024];
+  __shared__ int32_t tmp[PM_THREADS];
+  const int E = p.n_experts;
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+    int32_t total = 0;
+    for (int b = 0; b < p.n_chunks; ++b) {
+      int32_t v = p.block_counts[b * E + e];
+      p.block_counts[b * E + e] = total;  // becomes the chunk's base inside expert e
+      total += v;
+    }
+    p.expert_counts[e] = total;
+    off[e] = total;
+  }
+  __syncthreads();
+  block_exclusive_scan(off, E, tmp);
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+    p.expert_offsets[e] = off[e];
+    for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];
+  }
+  if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
+}
+
+// Pass 3: stable placement of each chunk from its base.
+__global__ __launch_bounds__(PM_THREADS) void permute_place_kernel(PermuteArgs p) {
+  __shared__ int32_t run[256];
+  __shared__ int32_t wc[PM_WAVES * 256];
+  const int E = p.n_experts;
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) run[e] = p.block_counts[blockIdx.x * E + e];
+  for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
+  __syncthreads();
+  const int64_t s0 = int64_t(blockIdx.x) * p.chunk;
+  const int64_t s1 = min<int64_t>(s0 + p.chunk, p.slots);
+  place_chunk(p.topk_idx, s0, s1, E, run, wc, p.sorted_slot, p.slot_pos);
+}
+
+// x_perm[r] = x[sorted_slot[r] / k], 16 bytes per lane.
+__global__ __launch_bounds__(PM_THREADS) void gather_rows_kernel(GatherArgs p) {
+  const int chunks = p.row_bytes / 16;
+  const int64_t total = p.rows * chunks;
+  for (int64_t i = int64_t(blockIdx.x) * PM_THREADS + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * PM_THREADS) {
+    const int64_t r = i / chunks;
+    const int c = static_cast<int>(i - r * chunks);
+    const int64_t src = p.sorted_slot[r] / p.div;
+    const i32x4_t v = *reinterpret_cast<const i32x4_t*>(
+        static_cast<const char*>(p.src) + src * p.row_bytes + c * 16);
+    *reinterpret_cast<i32x4_t*>(static_cast<char*>(p.dst) + r * p.row_bytes + c * 16) = v;
+  }
+}
+
+// M-tile schedule of a grouped GEMM: entry i = (group, first row) of the i-th
+// tile of `bm` rows; tiles of one group are consecutive, groups in order.
+// sched[0] = number of tiles, entries from sched + 2.
+__global__ __launch_bounds__(PM_THREADS) void schedule_kernel(ScheduleArgs p) {
+  __shared__ int32_t tiles[1024];
+  __shared__ int32_t tmp[PM_THREADS];
+  __shared__ int32_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  for (int g0 = 0; g0 < p.n_groups; g0 += 1024) {
+    const int n = min(1024, p.n_groups - g0);
+    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
+      const int g = g0 + i;
+      // no offsets: a single group spans every row
+      const int64_t a = p.offsets ? min<int64_t>(max(p.offsets[g], 0), p.rows) : 0;
+      const int64_t b = p.offsets ? min<int64_t>(max(p.offsets[g + 1], 0), p.rows) : p.rows;
+      tiles[i] = b > a ? static_cast<int32_t>((b - a + p.bm - 1) / p.bm) : 0;
+    }
+    __syncthreads();
+    const int32_t total = block_exclusive_scan(tiles, n, tmp);
+    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
+      const int g = g0 + i;
+      // no offsets: a single group spans every row
+      const int64_t a = p.offsets ? min<int64_t>(max(p.offsets[g], 0), p.rows) : 0;
+      const int64_t b = p.offsets ? min<int64_t>(max(p.offsets[g + 1], 0), p.rows) : p.rows;
+      int32_t at = carry + tiles[i];
+      for (int64_t m = a; m < b; m += p.bm, ++at) {
+        if (at < p.max_tiles) {
+          p.sched[2 + 2 * at] = g;
+          p.sched[3 + 2 * at] = static_cast<int32_t>(m);
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) carry += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) p.sched[0] = min(carry, p.max_tiles);
+}
+
+// y[t] = sum_j w[t,j] * y_perm[slot_pos[t*k+j]] (+ shared[t]), fp32, rounded once.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
+  const int64_t t = blockIdx.x;
+  const int k = p.top_k;
+  const int d4 = p.hidden / 4;
+  __shared__ int32_t pos[64];
+  __shared__ float w[64];
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = p.slot_pos[t * k + threadIdx.x];
+    w[threadIdx.x] = p.topk_w[t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d4; c += PM_THREADS) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.y_perm + int64_t(pos[j]) * p.hidden + c * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w[j], v[q], acc[q]);
+    }
+    if (p.shared) {
+      const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.shared + t * p.hidden + c * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = acc[q] + sv[q];
+    }
+    if (BF16_OUT) {
+      uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+      uint32_t hi = f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+      reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.hidden)[c] = make_uint2(lo, hi);
+    } else {
+      reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.hidden)[c] = acc;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream) {
+  if (p.n_chunks <= 1) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(permute_hist_kernel, dim3(p.n_chunks), dim3(PM_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
+    hipLaunchKernelGGL(permute_place_kernel, dim3(p.n_chunks), dim3(PM_THREADS), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& p, hipStream_t stream) {
+  const int64_t total = p.rows * (p.row_bytes / 16);
+  int64_t blocks = (total + PM_THREADS - 1) / PM_THREADS;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(PM_THREADS), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream) {
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream) {
+  dim3 grid(static_cast<unsigned>(p.tokens));
+  if (bf16_out)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(PM_THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(PM_THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace moe

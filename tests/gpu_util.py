@@ -1,0 +1,54 @@
+"""Helpers for the GPU parity tests: upload seeded inputs and compare with the oracle."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from non_gated_relu_amd import binding
+
+# Output tolerance, as fractions of the oracle output's RMS (bf16 output,
+# fp32 accumulation): max-abs 2e-2 and mean-abs 2e-3.
+MAX_TOL = 2e-2
+MEAN_TOL = 2e-3
+# Routing weights: fp32-accumulated logits differ from fp64 by up to a few
+# 1e-6 at d = 2688; ds/s = (1 - s) dl, and w = s / sum(s) doubles that at
+# most, plus a few fp32 ulps of the normalisation: below 1e-5 relative.
+W_RTOL = 1e-5
+
+
+def upload(inp: dict, wl, device="cuda"):
+    return {k: binding.to_device(v, device, k, wl) for k, v in inp.items() if v is not None}
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rms(a) -> float:
+    return float(np.sqrt(np.mean(np.square(np.asarray(a, np.float64)))))
+
+
+def assert_close_rms(got, ref, what: str, max_tol=MAX_TOL, mean_tol=MEAN_TOL, R=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    R = rms(ref) if R is None else R
+    err = np.abs(got - ref)
+    mx, mn = err.max() / R, err.mean() / R
+    print(f"{what}: max/R={mx:.3e} mean/R={mn:.3e} R={R:.4g}", flush=True)
+    assert mx <= max_tol, f"{what}: max-abs error {mx:.3e} of RMS exceeds {max_tol}"
+    assert mn <= mean_tol, f"{what}: mean-abs error {mn:.3e} of RMS exceeds {mean_tol}"
+
+
+def assert_routing_equal(gpu_idx, gpu_w, ref_idx, ref_w, margin, what: str):
+    gi = gpu_idx.cpu().numpy()
+    bad = np.flatnonzero((gi != ref_idx).any(axis=1))
+    if bad.size:
+        lines = [f"token {t}: gpu {gi[t].tolist()} oracle {ref_idx[t].tolist()} "
+                 f"margin {margin[t]:.3e}" for t in bad[:10]]
+        raise AssertionError(f"{what}: {bad.size} tokens routed differently\n" + "\n".join(lines))
+    gw = gpu_w.cpu().numpy().astype(np.float64)
+    rel = np.abs(gw - ref_w) / np.abs(ref_w)
+    print(f"{what}: routing exact, weight max rel err {rel.max():.3e}, "
+          f"min margin {margin.min():.3e}", flush=True)
+    assert rel.max() <= W_RTOL, f"{what}: weight rel err {rel.max():.3e}"

@@ -1,0 +1,185 @@
+"""GPU parity: every libmoe entry point against the fp64 oracle, at sizes the
+oracle finishes in seconds (several tiles, ragged tails, edge cases)."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (assert_close_rms, assert_routing_equal, rms, to_f64, upload)
+from non_gated_relu_amd import binding
+from non_gated_relu_amd.synthetic import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+# Ragged shapes: T not a multiple of 16, I and Is leaving partial 128-wide N tiles.
+RAGGED_BF16 = Workload("ragged-bf16-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "bf16", seed=21)
+RAGGED_FP8 = Workload("ragged-fp8-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "fp8", seed=22)
+PLAIN_TOPK = Workload("one-group-T40", 40, 128, 16, 1, 1, 5, 64, 128, "bf16", "bf16", seed=23)
+ALL_GROUPS = Workload("all-groups-T33", 33, 128, 64, 8, 8, 8, 128, 64, "bf16", "bf16", seed=24)
+WHOLE_GROUP = Workload("k-fills-group-T50", 50, 128, 32, 4, 1, 8, 64, 0, "bf16", "bf16", seed=25)
+BIG_ROWS = Workload("many-rows-T600", 600, 128, 16, 2, 1, 2, 128, 128, "bf16", "bf16", seed=26)
+SINGLE = dataclasses.replace(WORKLOADS["decode-bf16-T32"], name="decode-bf16-T1", tokens=1)
+
+SMALL = [WORKLOADS["tiny-f32-T64"], RAGGED_BF16, RAGGED_FP8, PLAIN_TOPK, ALL_GROUPS, WHOLE_GROUP,
+         BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    binding.lib()
+
+
+def _tol(wl):
+    # fp32 end to end: only accumulation order differs from fp64
+    return dict(max_tol=1e-4, mean_tol=1e-5) if wl.act_dtype == "f32" else {}
+
+
+def _layer_parts(wl, t, cfg):
+    T = t["x"].shape[0]
+    idx, w = binding.route(cfg, t["x"], t["w_gate"], t["e_bias"])
+    perm = binding.permute(cfg, idx, t["x"], with_x_perm=True)
+    y_perm = binding.expert_ffn(cfg, t["w_up"], t["w_down"], t["x"], perm["offsets"], T * wl.top_k,
+                                row_index=perm["sorted_slot"], index_div=wl.top_k,
+                                w_dtype=wl.expert_dtype, w_up_scale=t.get("w_up_scale"),
+                                w_down_scale=t.get("w_down_scale"))
+    shared = None
+    if wl.shared_inter:
+        off = torch.tensor([0, T], dtype=torch.int32, device=t["x"].device)
+        shared = binding.expert_ffn(cfg, t["ws_up"][None], t["ws_down"][None], t["x"], off, T,
+                                    w_dtype=wl.act_dtype)
+    y = binding.combine(cfg, perm["slot_pos"], w, y_perm, shared)
+    return dict(idx=idx, w=w, perm=perm, y_perm=y_perm, shared=shared, y=y)
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_small_layer_every_entry_point(wl):
+    print(f"case {wl.name}", flush=True)
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    cfg = binding.config_from(wl)
+    ref = oracle.forward(wl, inp)
+    T, k = wl.tokens, wl.top_k
+
+    parts = _layer_parts(wl, t, cfg)
+    torch.cuda.synchronize()
+    # route: exact ids, weights within rounding
+    assert_routing_equal(parts["idx"], parts["w"], ref["topk_idx"], ref["topk_w"], ref["margin"],
+                         wl.name)
+    # permute: exact against the stable grouping of the same ids
+    counts, offsets, sorted_slot, slot_pos = oracle.permute(parts["idx"].cpu().numpy(),
+                                                            wl.n_experts)
+    p = parts["perm"]
+    np.testing.assert_array_equal(p["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(p["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(p["sorted_slot"].cpu().numpy(), sorted_slot)
+    np.testing.assert_array_equal(p["slot_pos"].cpu().numpy(), slot_pos)
+    xs = t["x"].view(torch.int16) if t["x"].dtype == torch.bfloat16 else t["x"]
+    xp = p["x_perm"].view(torch.int16) if p["x_perm"].dtype == torch.bfloat16 else p["x_perm"]
+    assert torch.equal(xp, xs[torch.from_numpy(sorted_slot // k).long().cuda()])
+    # routed expert MLPs, row by row
+    rows = sorted_slot // k
+    mats = parts["idx"].cpu().numpy().reshape(-1)[sorted_slot]
+    ffn_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, rows, mats, inp["w_up"], inp["w_down"],
+                              wl.expert_dtype, inp["w_up_scale"], inp["w_down_scale"],
+                              quant_a=wl.expert_dtype == "fp8")
+    assert_close_rms(to_f64(parts["y_perm"]), ffn_ref, f"{wl.name} expert_ffn", **_tol(wl))
+    if wl.shared_inter:
+        sh_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, np.arange(T), np.zeros(T),
+                                 inp["ws_up"][None], inp["ws_down"][None], wl.act_dtype)
+        assert_close_rms(to_f64(parts["shared"]), sh_ref, f"{wl.name} shared", **_tol(wl))
+    # combine: only the final rounding separates it from the fp64 sum of its inputs
+    comb_ref = oracle.combine(parts["w"].cpu().numpy(), to_f64(parts["y_perm"]), slot_pos,
+                              None if parts["shared"] is None else to_f64(parts["shared"]))
+    got = to_f64(parts["y"])
+    ulp = 2.0 ** -8 if wl.act_dtype == "bf16" else 2.0 ** -22
+    assert (np.abs(got - comb_ref) <= ulp * np.abs(comb_ref) + 1e-6 * rms(comb_ref)).all()
+    # the layer against the oracle
+    assert_close_rms(got, ref["y"], f"{wl.name} layer", **_tol(wl))
+
+    # the fused entry point equals the composition bit for bit
+    y = binding.forward(cfg, t["x"], t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
+                        t.get("ws_up"), t.get("ws_down"), t.get("w_up_scale"),
+                        t.get("w_down_scale"))
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                       parts["y"].view(torch.int16) if y.dtype == torch.bfloat16 else parts["y"])
+
+
+def _bits(y):
+    return y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)
+
+
+@pytest.mark.parametrize("wl", [RAGGED_BF16, RAGGED_FP8, WORKLOADS["tiny-f32-T64"]],
+                         ids=lambda w: w.name)
+def test_deterministic_and_token_permutation_equivariant(wl):
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    layer = binding.MoELayer(wl, inp)
+    y1 = layer(t["x"]).clone()
+    y2 = layer(t["x"]).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y1), _bits(y2))
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(wl.tokens)).long().cuda()
+    y3 = layer(t["x"][perm].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y3), _bits(y1)[perm])
+
+
+def test_exact_ties_go_to_the_lowest_index():
+    wl = RAGGED_BF16
+    inp = make_inputs(wl)
+    inp["w_gate"] = np.zeros_like(inp["w_gate"])
+    inp["e_bias"] = np.zeros_like(inp["e_bias"])
+    t = upload(inp, wl)
+    idx, w = binding.route(binding.config_from(wl), t["x"], t["w_gate"], t["e_bias"])
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == np.arange(wl.top_k)).all()
+    np.testing.assert_allclose(w.cpu().numpy(), 2.5 / wl.top_k, rtol=1e-7)
+
+
+def test_zero_tokens_and_growing_calls_reuse_one_workspace():
+    wl = RAGGED_BF16
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    layer = binding.MoELayer(wl, inp)
+    empty = t["x"][:0]
+    y0 = torch.empty((0, wl.hidden), dtype=torch.bfloat16, device="cuda")
+    layer(empty, y=y0)
+    ref = oracle.forward(wl, inp)
+    for T in (1, 5, 77):
+        y = layer(t["x"][:T].contiguous())
+        torch.cuda.synchronize()
+        assert_close_rms(to_f64(y), ref["y"][:T], f"T={T}", R=rms(ref["y"]))
+
+
+def test_unnormalised_weights_and_other_scale():
+    wl = Workload("unnorm-T40", 40, 128, 16, 4, 2, 3, 64, 64, "bf16", "bf16",
+                  norm_topk_prob=False, routed_scaling_factor=1.5, seed=27)
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    ref = oracle.forward(wl, inp)
+    y = binding.MoELayer(wl, inp)(t["x"])
+    torch.cuda.synchronize()
+    assert_close_rms(to_f64(y), ref["y"], wl.name)
+
+
+def test_identical_experts_reduce_to_one_dense_mlp():
+    wl = RAGGED_BF16
+    inp = make_inputs(wl)
+    inp["w_up"][:] = inp["w_up"][5]
+    inp["w_down"][:] = inp["w_down"][5]
+    t = upload(inp, wl)
+    y = binding.MoELayer(wl, inp)(t["x"])
+    # every token: 2.5 * FFN_5(x) + S(x), whatever the routing
+    T = wl.tokens
+    ffn = oracle.ffn_rows(inp["x"], "bf16", np.arange(T), np.full(T, 5), inp["w_up"],
+                          inp["w_down"], "bf16")
+    sh = oracle.ffn_rows(inp["x"], "bf16", np.arange(T), np.zeros(T), inp["ws_up"][None],
+                         inp["ws_down"][None], "bf16")
+    torch.cuda.synchronize()
+    assert_close_rms(to_f64(y), 2.5 * ffn + sh, "identical experts")
