@@ -1,0 +1,257 @@
+"""Benchmark of the Nemotron-H MoE layer forward on one MI355X.
+
+One step = one ``moe_forward`` call (route -> permute -> routed expert MLPs ->
+shared expert -> combine) over one batch of seeded synthetic tokens that are
+already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The default workload is the Nemotron-H decode step (T=32, d=2688, 128 experts
+in 8 groups, top-6 from one group, I=1856, shared 3712, bf16).  Besides
+tokens/s the line carries the roofline of the dominant kernel, timed live
+with per-kernel HIP events on the stream the kernels run on, and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; TFLOP/s and HBM GB/s as % of MI355X peak"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "decode-bf16-T32"
+DEFAULT_STEPS = {"tiny-f32-T64": 200, "decode-bf16-T32": 200, "prefill-bf16-T4096": 50,
+                 "skew-bf16-T16384": 20, "fp8-T8192": 30}
+# kernels whose counter readings are reported as "traffic"
+TRAFFIC_SOURCES = ["non_gated_relu_amd/csrc/gemm.hip", "non_gated_relu_amd/csrc/common.hpp",
+                   "non_gated_relu_amd/csrc/internal.hpp"]
+
+
+def esize(dt):
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dt]
+
+
+def stage_work(wl, active: int):
+    """Algorithmic bytes and flops of each stage's launch(es) for one step.
+
+    Bytes count what the method must move: the weights of the active experts
+    (one unit = one expert projection of I*d elements, plus its fp32 row
+    scales when fp8), the stage's input activations and its outputs.
+    """
+    T, d, E, k, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
+    S = T * k
+    we, ae = esize(wl.expert_dtype), esize(wl.act_dtype)
+    fp8 = wl.expert_dtype == "fp8"
+    a_in = 1 if fp8 else ae              # the routed GEMMs read x (fp8: its e4m3 codes)
+    h_out = 4 if fp8 else (4 if wl.expert_dtype == "f32" else 2)  # h as written by the up GEMM
+    h_in = 1 if fp8 else h_out
+    scale_up = active * I * 4 if fp8 else 0
+    scale_dn = active * d * 4 if fp8 else 0
+    w = {
+        "route": dict(bytes=T * d * ae + E * d * ae + E * 4 + S * 8, flops=2 * T * d * E,
+                      dtype=wl.act_dtype),
+        "routed_up": dict(bytes=active * I * d * we + scale_up + T * d * a_in + S * I * h_out,
+                          flops=2 * S * d * I, dtype=wl.expert_dtype, unit_bytes=I * d * we,
+                          units=active),
+        "routed_down": dict(bytes=active * d * I * we + scale_dn + S * I * h_in + S * d * 4,
+                            flops=2 * S * I * d, dtype=wl.expert_dtype, unit_bytes=d * I * we,
+                            units=active),
+    }
+    if Is:
+        w["shared_up"] = dict(bytes=Is * d * ae + T * d * ae + T * Is * ae, flops=2 * T * d * Is,
+                              dtype=wl.act_dtype, unit_bytes=Is * d * ae, units=1)
+        w["shared_down"] = dict(bytes=d * Is * ae + T * Is * ae + T * d * 4, flops=2 * T * Is * d,
+                                dtype=wl.act_dtype, unit_bytes=d * Is * ae, units=1)
+    w["combine"] = dict(bytes=S * d * 4 + T * d * 4 * (1 if Is else 0) + T * d * ae + S * 8,
+                        flops=0, dtype="f32")
+    return w
+
+
+def layer_work(wl, active: int):
+    """Algorithmic flops and bytes of one whole layer step."""
+    T, d, E, k, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
+    we, ae = esize(wl.expert_dtype), esize(wl.act_dtype)
+    flops = T * (2 * d * E + k * 4 * d * I + 4 * d * Is)
+    scales = active * (I + d) * 4 if wl.expert_dtype == "fp8" else 0
+    byts = active * 2 * I * d * we + scales + 2 * Is * d * ae + E * d * ae + E * 4 + 2 * T * d * ae
+    return flops, byts
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str, kernel_stage: str):
+    """HBM bytes per launch from committed counter readings, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(workload, {}).get(kernel_stage)
+    if not entry or entry.get("source_sha256") != source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, y_gpu, idx_gpu, budget_s: float):
+    """The oracle on the bench's own tokens, repeated for about budget_s seconds."""
+    import numpy as np
+
+    import oracle
+
+    T = wl.tokens
+    n = min(T, 32)
+    tokens = np.arange(n)
+    reps, elapsed, out = 0, 0.0, None
+    t0 = time.perf_counter()
+    while reps == 0 or (elapsed < budget_s and reps < 1000):
+        out = oracle.forward(wl, inp, tokens=tokens)
+        reps += 1
+        elapsed = time.perf_counter() - t0
+    R = float(np.sqrt(np.mean(out["y"] ** 2)))
+    err = np.abs(y_gpu[:n].astype(np.float64) - out["y"])
+    parity = {"tokens_checked": n, "max_over_rms": float(err.max() / R),
+              "mean_over_rms": float(err.mean() / R),
+              "routing_exact": bool(np.array_equal(idx_gpu[:n], out["topk_idx"]))}
+    base = {"value": n * reps / elapsed, "unit": "tokens/s",
+            "cores": int(oracle.lib().orc_num_threads()), "kind": "oracle",
+            "sample": f"fp64 oracle on the first {n} tokens of this workload, "
+                      f"{reps} repetition(s), {elapsed:.1f} s wall"}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 10 device-to-device copies of this many bytes (a "
+                         "reference kernel for calibrating HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_bytes:
+        import torch
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 10}))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from non_gated_relu_amd import binding
+    from non_gated_relu_amd.synthetic import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[args.workload]
+    steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    print(f"bench: generating {wl.name}", file=sys.stderr, flush=True)
+    inp = make_inputs(wl)
+    layer = binding.MoELayer(wl, inp, device=dev)
+    x = binding.to_device(inp["x"], dev, "x", wl)
+    y = torch.empty((wl.tokens, wl.hidden), dtype=x.dtype, device=dev)
+    stages = binding.stages_of(wl)
+    # one set of kernel timestamp events per timed step, read after the region
+    evs = [binding.StageEvents() for _ in range(steps)]
+
+    print(f"bench: warmup {args.warmup}, timing {steps} steps", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        layer(x, y=y, stage_events=evs[i % steps])
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for i in range(steps):
+        layer(x, y=y, stage_events=evs[i])
+    torch.cuda.synchronize()
+    total_s = time.perf_counter() - t0
+
+    per_stage = {s: 0.0 for s in stages}
+    for e in evs:
+        for s, ms in e.elapsed_ms(stages).items():
+            per_stage[s] += ms
+    stage_ms = {s: per_stage[s] / steps for s in stages}
+
+    counts = layer.expert_counts.cpu().numpy()
+    active = int((counts > 0).sum())
+    work = stage_work(wl, active)
+    ms_per_step = 1e3 * total_s / steps
+    tokens_per_s = wl.tokens * steps / total_s
+
+    # dominant kernel: the GEMM stage with the largest device time
+    gemm_stages = [s for s in stages if s in work and work[s]["flops"] > 0 and s != "route"]
+    dom = max(gemm_stages, key=lambda s: stage_ms[s])
+    dw = work[dom]
+    t_s = stage_ms[dom] / 1e3
+    peak_t = PEAK_TFLOPS[dw["dtype"]]
+    hbm_bound = dw["bytes"] / (PEAK_HBM_GBS * 1e9) >= dw["flops"] / (peak_t * 1e12)
+    if hbm_bound:
+        achieved, peak, unit = dw["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = dw["flops"] / t_s / 1e12, peak_t, "TFLOP/s"
+    roofline = {"bound": "hbm" if hbm_bound else "mfma", "achieved": achieved, "peak": peak,
+                "unit": unit, "frac": achieved / peak, "traffic": load_traffic(wl.name, dom),
+                "kernel": dom, "kernel_ms": stage_ms[dom],
+                "algorithmic_bytes_per_launch": dw["bytes"],
+                "algorithmic_flops_per_launch": dw["flops"]}
+    if "unit_bytes" in dw:
+        roofline["units_per_launch"] = dw["units"]
+        roofline["unit_bytes"] = dw["unit_bytes"]
+
+    flops, byts = layer_work(wl, active)
+    layer_fig = {"tflops": flops / total_s * steps / 1e12,
+                 "tflops_frac_bf16_peak": flops / total_s * steps / 1e12 / PEAK_TFLOPS["bf16"],
+                 "hbm_gbs": byts / total_s * steps / 1e9,
+                 "hbm_frac": byts / total_s * steps / 1e9 / PEAK_HBM_GBS,
+                 "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": byts,
+                 "active_experts": active}
+
+    line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "fp8+bf16" if wl.expert_dtype == "fp8" else wl.act_dtype,
+            "data": "synthetic (seeded Gaussian inputs and weights)",
+            "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,
+                       "experts": wl.n_experts, "groups": wl.n_group,
+                       "topk_group": wl.topk_group, "top_k": wl.top_k, "inter": wl.inter,
+                       "shared_inter": wl.shared_inter, "expert_dtype": wl.expert_dtype,
+                       "parallelism": "single GPU"},
+            "roofline": roofline, "layer": layer_fig,
+            "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
+    if args.cpu_seconds > 0:
+        y_np = y.float().cpu().numpy()
+        idx_np = layer.topk_idx[:wl.tokens].cpu().numpy()
+        line["cpu_baseline"], line["parity"] = cpu_baseline(wl, inp, y_np, idx_np,
+                                                            args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

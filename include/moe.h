@@ -167,6 +167,33 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
                        int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* Measurement variant of moe_forward: the same launches and results.  When
+ * `stage_events` is not NULL it holds 2 * MOE_T_SLOTS hipEvent_t created by
+ * the caller (entries may be NULL); the kernels of stage i are launched with
+ * stage_events[2i] recording the start of the stage's first kernel and
+ * stage_events[2i+1] the end of its last one (hipExtLaunchKernelGGL), so
+ * hipEventElapsedTime of the pair is the stage's device time.  Stages that do
+ * not run for the configuration leave their events untouched. */
+enum {
+  MOE_T_ROUTE = 0,        /* router + grouped top-k                       */
+  MOE_T_PERMUTE = 1,      /* histogram, scan, stable placement            */
+  MOE_T_QUANT_X = 2,      /* fp8 experts: per-token e4m3 quantisation of x */
+  MOE_T_ROUTED_UP = 3,    /* routed up GEMM + relu^2                      */
+  MOE_T_QUANT_H = 4,      /* fp8 experts: per-row e4m3 quantisation of h  */
+  MOE_T_ROUTED_DOWN = 5,  /* routed down GEMM                             */
+  MOE_T_SHARED_UP = 6,    /* shared-expert up GEMM + relu^2               */
+  MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM                      */
+  MOE_T_COMBINE = 8,      /* weighted combine + output rounding           */
+  MOE_T_SLOTS = 9
+};
+moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
+                             const void* w_gate, const float* e_bias, const void* w_up,
+                             const float* w_up_scale, const void* w_down,
+                             const float* w_down_scale, const void* ws_up, const void* ws_down,
+                             void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* stage_events);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);
 

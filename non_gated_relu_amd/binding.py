@@ -67,9 +67,10 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_forward.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [_vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
-                     "moe_forward"):
+                     "moe_forward", "moe_forward_timed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,18 +193,55 @@ def combine(cfg: MoeConfig, slot_pos, topk_w, y_perm, shared_out=None, y=None):
     return y
 
 
+STAGES = ("route", "permute", "quant_x", "routed_up", "quant_h", "routed_down", "shared_up",
+          "shared_down", "combine")
+
+
 def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_up_scale=None,
-            w_down_scale=None, ws=None, y=None, topk_idx=None, topk_w=None, expert_counts=None):
+            w_down_scale=None, ws=None, y=None, topk_idx=None, topk_w=None, expert_counts=None,
+            stage_events=None):
+    """moe_forward; with ``stage_events`` (a StageEvents) moe_forward_timed."""
     T = x.shape[0]
     if y is None:
         y = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
     if ws is None:
         ws = workspace(workspace_size(cfg, T), x)
-    _check(lib().moe_forward(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(w_up),
-                             _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(ws_up),
-                             _p(ws_down), _p(y), _p(topk_idx), _p(topk_w), _p(expert_counts),
-                             _p(ws), ws.numel(), _stream()), "moe_forward")
+    args = [ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(w_up), _p(w_up_scale),
+            _p(w_down), _p(w_down_scale), _p(ws_up), _p(ws_down), _p(y), _p(topk_idx),
+            _p(topk_w), _p(expert_counts), _p(ws), ws.numel(), _stream()]
+    if stage_events is None:
+        _check(lib().moe_forward(*args), "moe_forward")
+    else:
+        _check(lib().moe_forward_timed(*args, stage_events.array), "moe_forward_timed")
     return y
+
+
+class StageEvents:
+    """One start/stop event pair per stage of moe_forward_timed."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(STAGES))]
+        for e in self.events:
+            e.record()  # materialise the underlying hipEvent_t
+        torch.cuda.synchronize()
+        self.array = (ctypes.c_void_p * len(self.events))(
+            *[ctypes.c_void_p(e.cuda_event) for e in self.events])
+    def elapsed_ms(self, stages):
+        """{stage: ms} of the listed stages (those that ran; call after a sync)."""
+        return {s: self.events[2 * STAGES.index(s)].elapsed_time(
+            self.events[2 * STAGES.index(s) + 1]) for s in stages}
+
+
+def stages_of(wl):
+    """The stages moe_forward runs for a workload."""
+    st = ["route", "permute"]
+    if wl.expert_dtype == "fp8":
+        st += ["quant_x", "routed_up", "quant_h", "routed_down"]
+    else:
+        st += ["routed_up", "routed_down"]
+    if wl.shared_inter:
+        st += ["shared_up", "shared_down"]
+    return st + ["combine"]
 
 
 class MoELayer:
@@ -227,7 +265,7 @@ class MoELayer:
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=self.device)
         self.expert_counts = torch.empty((wl.n_experts,), dtype=torch.int32, device=self.device)
 
-    def __call__(self, x, y=None):
+    def __call__(self, x, y=None, stage_events=None):
         T = x.shape[0]
         if T > self.max_tokens:
             raise ValueError(f"{T} tokens exceed the workspace sized for {self.max_tokens}")
@@ -235,7 +273,8 @@ class MoELayer:
         return forward(self.cfg, x, t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
                        t.get("ws_up"), t.get("ws_down"), t.get("w_up_scale"),
                        t.get("w_down_scale"), ws=self.ws, y=y, topk_idx=self.topk_idx[:T],
-                       topk_w=self.topk_w[:T], expert_counts=self.expert_counts)
+                       topk_w=self.topk_w[:T], expert_counts=self.expert_counts,
+                       stage_events=stage_events)
 
 
 def to_device(a, device, name: str, wl):

@@ -280,24 +280,23 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
 }
 
 template <int KIND, int EPI>
-hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream) {
+hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
+                           Timing t) {
   if (shape.bm == 16)
-    hipLaunchKernelGGL((gemm_kernel<KIND, 16, 128, 1, 4, EPI>), dim3(grid), dim3(G_THREADS), 0,
-                       stream, p);
-  else if (shape.bm == 64)
-    hipLaunchKernelGGL((gemm_kernel<KIND, 64, 128, 2, 2, EPI>), dim3(grid), dim3(G_THREADS), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL((gemm_kernel<KIND, 128, 128, 2, 2, EPI>), dim3(grid), dim3(G_THREADS), 0,
-                       stream, p);
-  return hipGetLastError();
+    return launch_k(gemm_kernel<KIND, 16, 128, 1, 4, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
+                    p);
+  if (shape.bm == 64)
+    return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
+                    p);
+  return launch_k(gemm_kernel<KIND, 128, 128, 2, 2, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
+                  p);
 }
 
 template <int KIND>
 hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned grid,
-                       hipStream_t stream) {
-  return epi == EPI_RELU2 ? launch_kind_epi<KIND, EPI_RELU2>(p, shape, grid, stream)
-                          : launch_kind_epi<KIND, EPI_PLAIN>(p, shape, grid, stream);
+                       hipStream_t stream, Timing t) {
+  return epi == EPI_RELU2 ? launch_kind_epi<KIND, EPI_RELU2>(p, shape, grid, stream, t)
+                          : launch_kind_epi<KIND, EPI_PLAIN>(p, shape, grid, stream, t);
 }
 
 }  // namespace
@@ -316,22 +315,20 @@ int64_t max_mtiles(int64_t rows, int groups, int bm) {
 }
 
 hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_bound,
-                       hipStream_t stream) {
+                       hipStream_t stream, Timing t) {
   const int64_t grid64 = mtiles_bound * p.n_tiles;
   if (grid64 <= 0) return hipSuccess;
   if (grid64 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>(grid64);
-  if (kind == K_FP8) return launch_kind<K_FP8>(p, epi, shape, grid, stream);
-  if (kind == K_BF16) return launch_kind<K_BF16>(p, epi, shape, grid, stream);
-  return launch_kind<K_F32>(p, epi, shape, grid, stream);
+  if (kind == K_FP8) return launch_kind<K_FP8>(p, epi, shape, grid, stream, t);
+  if (kind == K_BF16) return launch_kind<K_BF16>(p, epi, shape, grid, stream, t);
+  return launch_kind<K_F32>(p, epi, shape, grid, stream, t);
 }
 
-hipError_t launch_quant(const QuantArgs& p, hipStream_t stream) {
+hipError_t launch_quant(const QuantArgs& p, hipStream_t stream, Timing t) {
   if (p.rows <= 0) return hipSuccess;
   const int64_t blocks = (p.rows + 3) / 4;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     p);
-  return hipGetLastError();
+  return launch_k(quant_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), stream, t, p);
 }
 
 }  // namespace moe

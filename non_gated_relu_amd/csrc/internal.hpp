@@ -1,9 +1,28 @@
 // internal.hpp -- argument blocks and launchers shared inside libmoe.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 
 namespace moe {
+
+// Optional kernel timestamps: a launch given events records its own start
+// and end (hipExtLaunchKernelGGL), adding no packets to the stream.
+struct Timing {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
+                           Timing t, Args... args) {
+  if (t.start || t.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  return hipGetLastError();
+}
 
 struct RouteArgs {
   const void* x;        // [tokens, d]
@@ -91,12 +110,12 @@ struct GemmShape {
   int bm, bn;
 };
 
-hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream);
-hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream);
+hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream, Timing t = {});
+hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t = {});
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream);
-hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream);
-hipError_t launch_quant(const QuantArgs& p, hipStream_t stream);
+hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t = {});
+hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream, Timing t = {});
+hipError_t launch_quant(const QuantArgs& p, hipStream_t stream, Timing t = {});
 
 // Pick the tile shape for a grouped GEMM with `rows` problem rows over
 // `groups` matrices.
@@ -105,6 +124,6 @@ GemmShape pick_gemm_shape(int kind, int64_t rows, int groups);
 int64_t max_mtiles(int64_t rows, int groups, int bm);
 // Launch one grouped GEMM (schedule already built for shape.bm).
 hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_bound,
-                       hipStream_t stream);
+                       hipStream_t stream, Timing t = {});
 
 }  // namespace moe

@@ -114,10 +114,16 @@ FfnBuffers carve_ffn(Carver& cv, int32_t w_dtype, int inter, int hidden, int64_t
   return b;
 }
 
+// Timing slots of one grouped MLP: quantise a, up GEMM, quantise h, down GEMM.
+struct FfnTiming {
+  Timing qa, up, qh, down;
+};
+
 moe_status run_ffn(const moe_config& c, int n_mats, int inter, int32_t w_dtype, int64_t a_rows,
                    const void* a, int64_t rows, const int32_t* offsets, const int32_t* row_index,
                    int index_div, const void* w_up, const float* up_scale, const void* w_down,
-                   const float* down_scale, float* out, const FfnBuffers& b, hipStream_t s) {
+                   const float* down_scale, float* out, const FfnBuffers& b, hipStream_t s,
+                   const FfnTiming& tm = FfnTiming{}) {
   if (rows == 0) return MOE_OK;
   const FfnPlan f = plan_ffn(w_dtype, rows, n_mats);
   hipError_t e;
@@ -128,7 +134,7 @@ moe_status run_ffn(const moe_config& c, int n_mats, int inter, int32_t w_dtype, 
   const float* a_sc = nullptr;
   if (kind == K_FP8) {
     QuantArgs q{a, b.aq, b.as, a_rows, c.hidden, 1, nullptr};
-    if ((e = launch_quant(q, s)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = launch_quant(q, s, tm.qa)) != hipSuccess) return MOE_ERR_HIP;
     a_op = b.aq;
     a_sc = b.as;
   }
@@ -148,13 +154,13 @@ moe_status run_ffn(const moe_config& c, int n_mats, int inter, int32_t w_dtype, 
   up.index_div = index_div;
   up.n_tiles = (inter + f.shape.bn - 1) / f.shape.bn;
   up.out_bf16 = w_dtype == MOE_BF16;
-  if ((e = launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s)) != hipSuccess)
+  if ((e = launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s, tm.up)) != hipSuccess)
     return MOE_ERR_HIP;
   const void* h_op = b.h;
   const float* h_sc = nullptr;
   if (kind == K_FP8) {
     QuantArgs q{b.h, b.hq, b.hs, rows, inter, 0, nullptr};
-    if ((e = launch_quant(q, s)) != hipSuccess) return MOE_ERR_HIP;
+    if ((e = launch_quant(q, s, tm.qh)) != hipSuccess) return MOE_ERR_HIP;
     h_op = b.hq;
     h_sc = b.hs;
   }
@@ -174,7 +180,7 @@ moe_status run_ffn(const moe_config& c, int n_mats, int inter, int32_t w_dtype, 
   dn.index_div = 1;
   dn.n_tiles = (c.hidden + f.shape.bn - 1) / f.shape.bn;
   dn.out_bf16 = 0;
-  if ((e = launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s)) != hipSuccess)
+  if ((e = launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -219,19 +225,25 @@ FwdBuffers carve_forward(Carver& cv, const moe_config& c, int64_t T) {
 }
 
 moe_status do_route(const moe_config& c, int64_t T, const void* x, const void* w_gate,
-                    const float* e_bias, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+                    const float* e_bias, int32_t* topk_idx, float* topk_w, hipStream_t s,
+                    Timing t = {}) {
   RouteArgs p{x, w_gate, e_bias, topk_idx, topk_w, T, c.hidden, c.n_experts, c.n_group,
               c.topk_group, c.top_k, c.norm_topk_prob, c.routed_scaling_factor};
-  return hip_status(launch_route(p, kind_of(c.act_dtype), s));
+  return hip_status(launch_route(p, kind_of(c.act_dtype), s, t));
 }
 
 moe_status do_permute(const moe_config& c, int64_t T, const int32_t* topk_idx, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
-                      int32_t* block_counts, hipStream_t s) {
+                      int32_t* block_counts, hipStream_t s, Timing t = {}) {
   const int64_t S = T * c.top_k;
   PermuteArgs p{topk_idx, counts, offsets, sorted_slot, slot_pos, block_counts, S,
                 PERMUTE_CHUNK, permute_chunks(S), c.n_experts};
-  return hip_status(launch_permute(p, s));
+  return hip_status(launch_permute(p, s, t));
+}
+
+Timing slot(void* const* ev, int i) {
+  if (!ev) return Timing{};
+  return Timing{static_cast<hipEvent_t>(ev[2 * i]), static_cast<hipEvent_t>(ev[2 * i + 1])};
 }
 
 }  // namespace
@@ -371,12 +383,13 @@ moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slo
   return hip_status(launch_combine(p, cfg->act_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
-                       const float* e_bias, const void* w_up, const float* w_up_scale,
-                       const void* w_down, const float* w_down_scale, const void* ws_up,
-                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
-                       int32_t* expert_counts, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
+                             const void* w_gate, const float* e_bias, const void* w_up,
+                             const float* w_up_scale, const void* w_down,
+                             const float* w_down_scale, const void* ws_up, const void* ws_down,
+                             void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* ev) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
@@ -405,22 +418,37 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
   int32_t* cnt = expert_counts ? expert_counts : b.counts;
   const int64_t S = tokens * c.top_k;
 
-  if ((st = do_route(c, tokens, x, w_gate, e_bias, idx, wts, s)) != MOE_OK) return st;
-  if ((st = do_permute(c, tokens, idx, cnt, b.offsets, b.sorted_slot, b.slot_pos, b.block_counts,
-                       s)) != MOE_OK)
+  if ((st = do_route(c, tokens, x, w_gate, e_bias, idx, wts, s, slot(ev, MOE_T_ROUTE))) != MOE_OK)
     return st;
+  if ((st = do_permute(c, tokens, idx, cnt, b.offsets, b.sorted_slot, b.slot_pos, b.block_counts,
+                       s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
+    return st;
+  FfnTiming rt{slot(ev, MOE_T_QUANT_X), slot(ev, MOE_T_ROUTED_UP), slot(ev, MOE_T_QUANT_H),
+               slot(ev, MOE_T_ROUTED_DOWN)};
   if ((st = run_ffn(c, c.n_experts, c.inter, c.expert_dtype, tokens, x, S, b.offsets,
                     b.sorted_slot, c.top_k, w_up, w_up_scale, w_down, w_down_scale, b.y_perm,
-                    b.routed, s)) != MOE_OK)
+                    b.routed, s, rt)) != MOE_OK)
     return st;
   if (c.shared_inter > 0) {
+    FfnTiming sh{Timing{}, slot(ev, MOE_T_SHARED_UP), Timing{}, slot(ev, MOE_T_SHARED_DOWN)};
     if ((st = run_ffn(c, 1, c.shared_inter, c.act_dtype, tokens, x, tokens, nullptr, nullptr, 1,
-                      ws_up, nullptr, ws_down, nullptr, b.shared_out, b.shared, s)) != MOE_OK)
+                      ws_up, nullptr, ws_down, nullptr, b.shared_out, b.shared, s, sh)) != MOE_OK)
       return st;
   }
   CombineArgs p{b.slot_pos, wts, b.y_perm, c.shared_inter > 0 ? b.shared_out : nullptr, y,
                 tokens, c.hidden, c.top_k};
-  return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s));
+  return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_COMBINE)));
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
+                       const float* e_bias, const void* w_up, const float* w_up_scale,
+                       const void* w_down, const float* w_down_scale, const void* ws_up,
+                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                       int32_t* expert_counts, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return moe_forward_timed(cfg, tokens, x, w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
+                           ws_up, ws_down, y, topk_idx, topk_w, expert_counts, workspace,
+                           workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

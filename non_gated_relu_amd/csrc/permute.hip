@@ -268,15 +268,18 @@ __global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
 
 }  // namespace
 
-hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream) {
-  if (p.n_chunks <= 1) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(permute_hist_kernel, dim3(p.n_chunks), dim3(PM_THREADS), 0, stream, p);
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
-    hipLaunchKernelGGL(permute_place_kernel, dim3(p.n_chunks), dim3(PM_THREADS), 0, stream, p);
-  }
-  return hipGetLastError();
+hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t) {
+  if (p.n_chunks <= 1)
+    return launch_k(permute_small_kernel, dim3(1), dim3(PM_THREADS), stream, t, p);
+  hipError_t e;
+  if ((e = launch_k(permute_hist_kernel, dim3(p.n_chunks), dim3(PM_THREADS), stream,
+                    Timing{t.start, nullptr}, p)) != hipSuccess)
+    return e;
+  if ((e = launch_k(permute_scan_kernel, dim3(1), dim3(PM_THREADS), stream, Timing{}, p)) !=
+      hipSuccess)
+    return e;
+  return launch_k(permute_place_kernel, dim3(p.n_chunks), dim3(PM_THREADS), stream,
+                  Timing{nullptr, t.stop}, p);
 }
 
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream) {
@@ -288,18 +291,14 @@ hipError_t launch_gather(const GatherArgs& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(PM_THREADS), 0, stream, p);
-  return hipGetLastError();
+hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t) {
+  return launch_k(schedule_kernel, dim3(1), dim3(PM_THREADS), stream, t, p);
 }
 
-hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream) {
+hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream, Timing t) {
   dim3 grid(static_cast<unsigned>(p.tokens));
-  if (bf16_out)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(PM_THREADS), 0, stream, p);
-  else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(PM_THREADS), 0, stream, p);
-  return hipGetLastError();
+  if (bf16_out) return launch_k(combine_kernel<true>, grid, dim3(PM_THREADS), stream, t, p);
+  return launch_k(combine_kernel<false>, grid, dim3(PM_THREADS), stream, t, p);
 }
 
 }  // namespace moe

@@ -176,13 +176,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs p) {
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream) {
+hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream, Timing t) {
   dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK));
-  if (kind == K_F32)
-    hipLaunchKernelGGL(route_kernel<K_F32>, grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL(route_kernel<K_BF16>, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  if (kind == K_F32) return launch_k(route_kernel<K_F32>, grid, dim3(256), stream, t, p);
+  return launch_k(route_kernel<K_BF16>, grid, dim3(256), stream, t, p);
 }
 
 }  // namespace moe

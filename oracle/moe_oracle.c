@@ -78,7 +78,20 @@ typedef struct {
   int32_t expert_dtype; /* routed weights */
 } orc_cfg;
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 int orc_version(void) { return 3; }
+
+/* Threads an OpenMP loop of the oracle uses. */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ codecs */
 
