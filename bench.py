@@ -67,10 +67,17 @@ def stage_work(wl, active: int):
                             units=active),
     }
     if Is:
-        w["shared_up"] = dict(bytes=Is * d * ae + T * d * ae + T * Is * ae, flops=2 * T * d * Is,
-                              dtype=wl.act_dtype, unit_bytes=Is * d * ae, units=1)
-        w["shared_down"] = dict(bytes=d * Is * ae + T * Is * ae + T * d * 4, flops=2 * T * Is * d,
-                                dtype=wl.act_dtype, unit_bytes=d * Is * ae, units=1)
+        sh_up = dict(bytes=Is * d * ae + T * d * ae + T * Is * ae, flops=2 * T * d * Is)
+        sh_dn = dict(bytes=d * Is * ae + T * Is * ae + T * d * 4, flops=2 * T * Is * d)
+        if wl.expert_dtype == wl.act_dtype:
+            # the shared expert runs inside the routed launches as one more group
+            for st, sh in (("routed_up", sh_up), ("routed_down", sh_dn)):
+                w[st]["bytes"] += sh["bytes"]
+                w[st]["flops"] += sh["flops"]
+                w[st]["shared_weight_bytes"] = Is * d * ae
+        else:
+            w["shared_up"] = dict(sh_up, dtype=wl.act_dtype, unit_bytes=Is * d * ae, units=1)
+            w["shared_down"] = dict(sh_dn, dtype=wl.act_dtype, unit_bytes=d * Is * ae, units=1)
     w["combine"] = dict(bytes=S * d * 4 + T * d * 4 * (1 if Is else 0) + T * d * ae + S * 8,
                         flops=0, dtype="f32")
     return w
@@ -142,6 +149,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the step replayed from a HIP graph)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 10 device-to-device copies of this many bytes (a "
                          "reference kernel for calibrating HBM byte counters)")
@@ -198,6 +207,21 @@ def main():
         for s, ms in e.elapsed_ms(stages).items():
             per_stage[s] += ms
     stage_ms = {s: per_stage[s] / steps for s in stages}
+    eager_s = total_s
+
+    # the same step replayed from a HIP graph: no per-kernel launch gaps
+    graph_s = None
+    if not args.no_graph:
+        gstep = binding.GraphStep(layer, x, y)
+        for _ in range(args.warmup):
+            gstep.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            gstep.replay()
+        torch.cuda.synchronize()
+        graph_s = time.perf_counter() - t0
+        total_s = graph_s
 
     counts = layer.expert_counts.cpu().numpy()
     active = int((counts > 0).sum())
@@ -224,6 +248,8 @@ def main():
     if "unit_bytes" in dw:
         roofline["units_per_launch"] = dw["units"]
         roofline["unit_bytes"] = dw["unit_bytes"]
+    if "shared_weight_bytes" in dw:
+        roofline["shared_weight_bytes_per_launch"] = dw["shared_weight_bytes"]
 
     flops, byts = layer_work(wl, active)
     layer_fig = {"tflops": flops / total_s * steps / 1e12,
@@ -243,6 +269,8 @@ def main():
                        "topk_group": wl.topk_group, "top_k": wl.top_k, "inter": wl.inter,
                        "shared_inter": wl.shared_inter, "expert_dtype": wl.expert_dtype,
                        "parallelism": "single GPU"},
+            "launch": "hipGraph replay of moe_forward" if graph_s else "eager moe_forward",
+            "eager_ms_per_step": 1e3 * eager_s / steps,
             "roofline": roofline, "layer": layer_fig,
             "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
     if args.cpu_seconds > 0:

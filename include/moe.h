@@ -91,7 +91,12 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t tokens, size_t* byt
  *   e_bias   [E]          fp32 correction bias, used only to select
  *   topk_idx [tokens, k]  int32 out, each row ascending by expert id
  *   topk_w   [tokens, k]  fp32 out, aligned with topk_idx
- * Logits accumulate in fp32; scores, group sums and comparisons are fp32. */
+ *   workspace optional: with at least moe_workspace_size(cfg, tokens) bytes,
+ *            large calls compute the logits as one GEMM into it; without, a
+ *            single kernel does all.  Both give the same bits.
+ * Logits accumulate in fp32, one MFMA per K step in ascending K; scores, group
+ * sums and comparisons are fp32.  A token's routing does not depend on the
+ * other tokens of the call. */
 moe_status moe_route(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
                      const float* e_bias, int32_t* topk_idx, float* topk_w, void* workspace,
                      size_t workspace_bytes, void* stream);
@@ -154,6 +159,8 @@ moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slo
 
 /* The whole layer: route -> permute -> routed expert MLPs -> shared expert ->
  * combine, bit-identical to that composition of the entry points above.
+ * When the shared expert's weights have the routed experts' type it runs in
+ * the routed GEMM launches as one extra group (same arithmetic per element).
  *   x [tokens, d], w_gate [E, d], e_bias [E] fp32, w_up [E, I, d], w_down [E, d, I]
  *   (expert_dtype; fp8 scales as in moe_expert_ffn), ws_up [Is, d], ws_down [d, Is]
  *   (act_dtype), y [tokens, d] act_dtype out.

@@ -136,13 +136,16 @@ def workspace(nbytes: int, like: torch.Tensor) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=like.device)
 
 
-def route(cfg: MoeConfig, x, w_gate, e_bias, topk_idx=None, topk_w=None):
+def route(cfg: MoeConfig, x, w_gate, e_bias, topk_idx=None, topk_w=None,
+          use_workspace: bool = True):
     T = x.shape[0]
     k = cfg.top_k
     topk_idx = _empty((T, k), torch.int32, x) if topk_idx is None else topk_idx
     topk_w = _empty((T, k), torch.float32, x) if topk_w is None else topk_w
+    ws = workspace(workspace_size(cfg, T), x) if use_workspace else None
     _check(lib().moe_route(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(topk_idx),
-                           _p(topk_w), None, 0, _stream()), "moe_route")
+                           _p(topk_w), _p(ws), 0 if ws is None else ws.numel(), _stream()),
+           "moe_route")
     return topk_idx, topk_w
 
 
@@ -233,13 +236,14 @@ class StageEvents:
 
 
 def stages_of(wl):
-    """The stages moe_forward runs for a workload."""
+    """The stages moe_forward runs for a workload (the shared expert has launches
+    of its own only when its weight type differs from the routed experts')."""
     st = ["route", "permute"]
     if wl.expert_dtype == "fp8":
         st += ["quant_x", "routed_up", "quant_h", "routed_down"]
     else:
         st += ["routed_up", "routed_down"]
-    if wl.shared_inter:
+    if wl.shared_inter and wl.expert_dtype != wl.act_dtype:
         st += ["shared_up", "shared_down"]
     return st + ["combine"]
 
@@ -275,6 +279,30 @@ class MoELayer:
                        t.get("w_down_scale"), ws=self.ws, y=y, topk_idx=self.topk_idx[:T],
                        topk_w=self.topk_w[:T], expert_counts=self.expert_counts,
                        stage_events=stage_events)
+
+
+class GraphStep:
+    """One MoELayer forward captured in a HIP graph (torch.cuda.CUDAGraph).
+
+    moe_forward allocates nothing and records no memset, so the captured
+    launch sequence replays as is; ``replay()`` recomputes ``y`` from the
+    current contents of ``x``.
+    """
+
+    def __init__(self, layer: MoELayer, x, y):
+        self.x, self.y = x, y
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer(x, y=y)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            layer(x, y=y)
+
+    def replay(self):
+        self.graph.replay()
+        return self.y
 
 
 def to_device(a, device, name: str, wl):

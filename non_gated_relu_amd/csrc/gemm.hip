@@ -12,11 +12,17 @@
 // reads 16 (or 32) contiguous bytes of one row.  A workgroup of 4 waves owns a
 // BM x BN output tile of one group (expert); its M tile comes from a schedule
 // built on the device from the group offsets, so the host never learns the
-// per-expert counts.  K is streamed in 128-byte stages through a double
-// buffer in LDS (rows padded to 144 bytes against bank conflicts): the next
-// stage's global loads are issued before the current stage's MFMAs.  A rows
-// are gathered through the routing permutation while loading, so the permuted
-// activations never exist in memory.
+// per-expert counts.  A rows are gathered through the routing permutation
+// while loading, so the permuted activations never exist in memory.
+//
+// K is streamed in 128-byte stages through a double buffer in LDS (rows
+// padded to 144 bytes against bank conflicts), the next stage's global loads
+// issued before the current stage's MFMAs.  Tile shapes: 16 x 128 for decode
+// (an expert sees a handful of tokens: each weight byte feeds one MFMA and
+// the launch is a weight stream), 64 x 128 and 128 x 128 for prefill.
+// Every output element accumulates its K steps in ascending order with the
+// same MFMA, whichever tile shape computes it, so results do not depend on
+// the launch configuration.
 #include "internal.hpp"
 
 namespace moe {
@@ -54,8 +60,9 @@ struct Frag<K_FP8> {
   using T = i32x8_t;
 };
 
+// Fragment bytes of one lane: p[0..FB) (LDS or global memory).
 template <int KIND>
-__device__ __forceinline__ typename Frag<KIND>::T lds_frag(const char* p) {
+__device__ __forceinline__ typename Frag<KIND>::T load_frag(const char* p) {
   if constexpr (KIND == K_FP8) {
     const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p);
     const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(p + 16);
@@ -79,8 +86,92 @@ __device__ __forceinline__ f32x4_t mma(typename Frag<KIND>::T a, typename Frag<K
     return mfma_f32x4(a, b, c);
 }
 
+// Which problem, group and rows a workgroup's tile covers.  The problem is
+// copied field by field with uniform selects: indexing the kernel-argument
+// array by a runtime value would move it to scratch memory.
+struct Tile {
+  GemmProblem p;
+  int g;        // group inside the problem
+  int64_t m0;   // first problem row
+  int64_t gend; // end of the group's rows
+  int n0;       // first output column
+};
+
+__device__ __forceinline__ GemmProblem pick_problem(const GemmArgs& pa, bool second) {
+  const GemmProblem& a = pa.prob[0];
+  const GemmProblem& b = pa.prob[1];
+  GemmProblem p;
+  p.a = second ? b.a : a.a;
+  p.a_scale = second ? b.a_scale : a.a_scale;
+  p.row_index = second ? b.row_index : a.row_index;
+  p.w = second ? b.w : a.w;
+  p.w_scale = second ? b.w_scale : a.w_scale;
+  p.offsets = second ? b.offsets : a.offsets;
+  p.out = second ? b.out : a.out;
+  p.a_rows = second ? b.a_rows : a.a_rows;
+  p.rows = second ? b.rows : a.rows;
+  p.n = second ? b.n : a.n;
+  p.k = second ? b.k : a.k;
+  p.index_div = second ? b.index_div : a.index_div;
+  p.out_bf16 = second ? b.out_bf16 : a.out_bf16;
+  return p;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t) {
+  const int mt = blockIdx.x / pa.n_tiles;
+  const int nt = blockIdx.x - mt * pa.n_tiles;
+  int gs;
+  if (pa.sched) {
+    if (mt >= pa.sched[0]) return false;
+    gs = pa.sched[2 + 2 * mt];
+    t.m0 = pa.sched[3 + 2 * mt];
+  } else {  // dense: one group, tiles in row order
+    gs = 0;
+    t.m0 = int64_t(mt) * BM;
+    if (t.m0 >= pa.prob[0].rows) return false;
+  }
+  // schedule group n_groups is the single group of the second problem
+  const bool second = gs >= pa.n_groups;
+  t.p = pick_problem(pa, second);
+  t.g = second ? 0 : gs;
+  const GemmProblem& p = t.p;
+  // no offsets: a single group spans every row
+  t.gend = p.offsets ? min<int64_t>(max<int64_t>(p.offsets[t.g + 1], 0), p.rows) : p.rows;
+  t.n0 = nt * BN;
+  return t.n0 < p.n;
+}
+
+__device__ __forceinline__ int64_t src_row(const GemmProblem& p, int64_t r) {
+  int64_t src = p.row_index ? int64_t(p.row_index[r]) / p.index_div : r;
+  return min<int64_t>(max<int64_t>(src, 0), p.a_rows - 1);
+}
+
+// Stores one 16x16 accumulator block: lane holds column `col`, rows r0..r0+3.
+template <int KIND, int EPI>
+__device__ __forceinline__ void store_block(const Tile& t, f32x4_t acc, int64_t r0, int col) {
+  const GemmProblem& p = t.p;
+  if (col >= p.n) return;
+  const float sw = KIND == K_FP8 ? p.w_scale[int64_t(t.g) * p.n + col] : 1.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t r = r0 + q;
+    if (r >= t.gend) return;
+    float v = acc[q];
+    if (KIND == K_FP8) v = (v * p.a_scale[src_row(p, r)]) * sw;
+    if (EPI == EPI_RELU2) {
+      v = fmaxf(v, 0.0f);
+      v = v * v;
+    }
+    if (p.out_bf16)
+      static_cast<uint16_t*>(p.out)[r * p.n + col] = f32_to_bf16(v);
+    else
+      static_cast<float*>(p.out)[r * p.n + col] = v;
+  }
+}
+
 template <int KIND, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs pa) {
   constexpr int ESZ = KindTraits<KIND>::ESZ;
   constexpr int STEP = KindTraits<KIND>::STEP;
   constexpr int FM = BM / WM / 16;
@@ -96,20 +187,12 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs p) {
   constexpr int STAGE = (BM + BN) * LDS_STRIDE;
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
+  Tile t;
+  if (!locate_tile<BM, BN>(pa, t)) return;
+  const GemmProblem& p = t.p;
   const int tid = threadIdx.x;
-  const int n_mt = p.sched[0];
-  const int mt = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x - mt * p.n_tiles;
-  if (mt >= n_mt) return;
-  const int g = p.sched[2 + 2 * mt];
-  const int64_t m0 = p.sched[3 + 2 * mt];
-  // no offsets: a single group spans every row
-  const int64_t gend =
-      p.offsets ? min<int64_t>(max<int64_t>(p.offsets[g + 1], 0), p.rows) : p.rows;
-  const int n0 = nt * BN;
-  if (n0 >= p.n) return;
   const int64_t kbytes = int64_t(p.k) * ESZ;
-  const char* wbase = static_cast<const char*>(p.w) + int64_t(g) * p.n * kbytes;
+  const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
   const int c16 = (tid % CPR) * 16;  // this thread's byte column inside a stage
 
   // source row of each chunk this thread loads (null = zero fill)
@@ -118,18 +201,15 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs p) {
 #pragma unroll
   for (int j = 0; j < CA; ++j) {
     const int row = tid / CPR + j * RPT;
-    const int64_t r = m0 + row;
-    a_src[j] = nullptr;
-    if (row < BM && r < gend) {
-      int64_t src = p.row_index ? int64_t(p.row_index[r]) / p.index_div : r;
-      src = min<int64_t>(max<int64_t>(src, 0), p.a_rows - 1);
-      a_src[j] = static_cast<const char*>(p.a) + src * kbytes + c16;
-    }
+    const int64_t r = t.m0 + row;
+    a_src[j] = (row < BM && r < t.gend)
+                   ? static_cast<const char*>(p.a) + src_row(p, r) * kbytes + c16
+                   : nullptr;
   }
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
     const int row = tid / CPR + j * RPT;
-    const int n = n0 + row;
+    const int n = t.n0 + row;
     b_src[j] = (row < BN && n < p.n) ? wbase + int64_t(n) * kbytes + c16 : nullptr;
   }
 
@@ -190,9 +270,9 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs p) {
     for (int ks = 0; ks < BKB / STEP; ++ks) {
       typename Frag<KIND>::T af[FM], bfr[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = lds_frag<KIND>(As + i * 16 * LDS_STRIDE + ks * STEP);
+      for (int i = 0; i < FM; ++i) af[i] = load_frag<KIND>(As + i * 16 * LDS_STRIDE + ks * STEP);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = lds_frag<KIND>(Bs + j * 16 * LDS_STRIDE + ks * STEP);
+      for (int j = 0; j < FN; ++j) bfr[j] = load_frag<KIND>(Bs + j * 16 * LDS_STRIDE + ks * STEP);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -202,36 +282,12 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs p) {
     __syncthreads();
   }
 
-  // epilogue: lane holds column lrow of each 16x16 block, rows 4*lgrp .. +3
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = m0 + wm * (BM / WM) + i * 16 + lgrp * 4 + q;
-      if (r >= gend) continue;
-      float sa = 1.0f;
-      if (KIND == K_FP8) {
-        int64_t src = p.row_index ? int64_t(p.row_index[r]) / p.index_div : r;
-        src = min<int64_t>(max<int64_t>(src, 0), p.a_rows - 1);
-        sa = p.a_scale[src];
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * (BN / WN) + j * 16 + lrow;
-        if (col >= p.n) continue;
-        float v = acc[i][j][q];
-        if (KIND == K_FP8) v = (v * sa) * p.w_scale[int64_t(g) * p.n + col];
-        if (EPI == EPI_RELU2) {
-          v = fmaxf(v, 0.0f);
-          v = v * v;
-        }
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[r * p.n + col] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[r * p.n + col] = v;
-      }
-    }
-  }
+    for (int j = 0; j < FN; ++j)
+      store_block<KIND, EPI>(t, acc[i][j], t.m0 + wm * (BM / WM) + i * 16 + lgrp * 4,
+                             t.n0 + wn * (BN / WN) + j * 16 + lrow);
 }
 
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.

@@ -30,10 +30,28 @@ struct RouteArgs {
   const float* e_bias;  // [E]
   int32_t* topk_idx;    // [tokens, k]
   float* topk_w;        // [tokens, k]
+  float* logits;        // [tokens, E] workspace (GEMM path), or null (one-kernel path)
   int64_t tokens;
   int hidden, n_experts, n_group, topk_group, top_k, norm_topk_prob;
   float scale;
 };
+
+// M-tile schedule of a grouped GEMM: sched[0] = tile count; entry i at
+// sched[2+2i] = group, sched[3+2i] = first problem row.  Tiles of a group are
+// consecutive and groups come in order; the optional extra group (index
+// n_groups) covers rows [0, extra_rows) of the second problem.
+struct ScheduleSpec {
+  int32_t* sched;      // [2 + 2*max_tiles], or null (no schedule wanted)
+  int64_t extra_rows;  // rows of the extra group (0 = none)
+  int bm;
+  int max_tiles;
+};
+
+// How the router gets its logits (route.hip).
+enum RouteMode : int { ROUTE_ONE_KERNEL = 0, ROUTE_WAVES = 1, ROUTE_GEMM = 2 };
+
+// Routing slots per permute workgroup (one workgroup does it all up to here).
+constexpr int PM_CHUNK = 4096;
 
 struct PermuteArgs {
   const int32_t* topk_idx;  // [slots]
@@ -43,9 +61,9 @@ struct PermuteArgs {
   int32_t* slot_pos;        // [slots]
   int32_t* block_counts;    // [n_chunks, E] workspace
   int64_t slots;
-  int64_t chunk;
-  int n_chunks;
+  int n_chunks;             // ceil(slots / PM_CHUNK)
   int n_experts;
+  ScheduleSpec sched;       // optional: schedule of the expert GEMMs
 };
 
 struct GatherArgs {
@@ -58,12 +76,10 @@ struct GatherArgs {
 };
 
 struct ScheduleArgs {
-  const int32_t* offsets;  // [n_groups+1]
-  int32_t* sched;          // [2 + 2*max_tiles]
+  const int32_t* offsets;  // [n_groups+1], or null: one group over all rows
   int64_t rows;
   int n_groups;
-  int bm;
-  int max_tiles;
+  ScheduleSpec spec;
 };
 
 struct CombineArgs {
@@ -78,21 +94,30 @@ struct CombineArgs {
 
 enum Epilogue : int { EPI_RELU2 = 0, EPI_PLAIN = 1 };
 
-struct GemmArgs {
+// One grouped GEMM problem: out[r] = epi(a[src(r)] . W[g]^T) for the rows r
+// of group g.
+struct GemmProblem {
   const void* a;             // [a_rows, K] operand rows (KIND elements)
   const float* a_scale;      // fp8: scale per a row, else null
-  const int32_t* row_index;  // problem row -> index, or null (identity)
+  const int32_t* row_index;  // problem row -> index (src = index / index_div), or null
   const void* w;             // [groups, N, K]
   const float* w_scale;      // fp8: [groups, N], else null
-  const int32_t* offsets;    // [groups+1] problem-row offsets
-  const int32_t* sched;      // M-tile schedule (see schedule_kernel)
+  const int32_t* offsets;    // [groups+1] problem-row offsets, or null: one group
   void* out;                 // [rows, N]
   int64_t a_rows;
   int64_t rows;
   int n, k;                  // N and K in elements
   int index_div;
-  int n_tiles;               // N tiles of the launch
   int out_bf16;              // epilogue stores bf16 (else fp32)
+};
+
+// A launch: the groups of prob[0], plus (schedule group index n_groups) the
+// single group of prob[1] when the schedule holds one.
+struct GemmArgs {
+  GemmProblem prob[2];
+  const int32_t* sched;
+  int n_groups;
+  int n_tiles;               // N tiles of the launch (the larger of the two problems)
 };
 
 struct QuantArgs {
@@ -102,7 +127,6 @@ struct QuantArgs {
   int64_t rows;
   int cols;
   int in_bf16;
-  const int32_t* valid_rows;  // optional device count: rows >= *valid_rows are skipped
 };
 
 // Tile shape of a grouped GEMM launch.
@@ -110,7 +134,10 @@ struct GemmShape {
   int bm, bn;
 };
 
-hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream, Timing t = {});
+// ROUTE_ONE_KERNEL computes logits and selects in one kernel; the other modes
+// put the logits in p.logits and then run the selection kernel.
+hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stream,
+                        Timing t = {});
 hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t = {});
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream);
 hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t = {});

@@ -9,17 +9,26 @@
 // "Requesting converter + runtime support for the Nemotron-H architecture"
 // (section "Architecture (config.json)").  Unsupported layers are refused up
 // front, as the exo sharding code refuses models it cannot handle.
+//
+// Launch sequence of moe_forward (one stream, no host synchronisation):
+//   route (1 kernel, or 2 for few tokens) -> permute (1 kernel for at most
+//   PM_CHUNK slots, else 3; it also writes the GEMM tile schedule) ->
+//   [fp8: quantise x] -> up GEMM + relu^2 -> [fp8: quantise h] -> down GEMM
+//   -> combine.  When the shared expert's weights have the routed experts'
+//   type it rides in the same two GEMM launches as one extra group; with fp8
+//   routed experts it gets its own two bf16 launches.
 #include <cmath>
 #include <cstring>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "internal.hpp"
 
 using namespace moe;
 
 namespace {
 
-constexpr int64_t PERMUTE_CHUNK = 4096;
+constexpr int64_t ROUTE_WAVES_MAX_TOKENS = 64;     // up to here: one wave per logit block
+constexpr int64_t ROUTE_DIRECT_MAX_TOKENS = 2048;  // beyond: router logits as a GEMM
 constexpr size_t ALIGN = 256;
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -75,175 +84,260 @@ struct Carver {
   }
 };
 
+Timing slot(void* const* ev, int i) {
+  if (!ev) return Timing{};
+  return Timing{static_cast<hipEvent_t>(ev[2 * i]), static_cast<hipEvent_t>(ev[2 * i + 1])};
+}
+
 // ------------------------------------------------------- grouped expert MLP
 
+// One family of expert MLPs: n_mats matrix pairs over grouped rows.
+struct Mlp {
+  int n_mats = 0;
+  int inter = 0;
+  int32_t w_dtype = MOE_BF16;
+  int64_t a_rows = 0;
+  const void* a = nullptr;
+  int64_t rows = 0;
+  const int32_t* offsets = nullptr;  // null: one group over all rows
+  const int32_t* row_index = nullptr;
+  int index_div = 1;
+  const void* w_up = nullptr;
+  const float* up_scale = nullptr;
+  const void* w_down = nullptr;
+  const float* down_scale = nullptr;
+  float* out = nullptr;
+  // workspace
+  void* h = nullptr;        // [rows, inter]: bf16 / fp32 (fp8: fp32 staging)
+  uint8_t* hq = nullptr;    // fp8 codes of h
+  float* hs = nullptr;      // fp8 row scales of h
+  uint8_t* aq = nullptr;    // fp8 codes of a
+  float* as = nullptr;      // fp8 row scales of a
+};
+
+// Shape and tile bound of a launch over `main` (+ `extra_rows` of a second
+// single-group problem).
 struct FfnPlan {
   GemmShape shape;
   int64_t mtiles;
 };
 
-FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats) {
+FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats, int64_t extra_rows) {
   FfnPlan f;
   f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats);
-  f.mtiles = max_mtiles(rows, n_mats, f.shape.bm);
+  f.mtiles = max_mtiles(rows, n_mats, f.shape.bm) +
+             (extra_rows > 0 ? (extra_rows + f.shape.bm - 1) / f.shape.bm : 0);
   return f;
 }
 
-struct FfnBuffers {
-  int32_t* sched;
-  void* h;        // [rows, inter]: bf16 / fp32 (fp8: fp32 staging)
-  uint8_t* hq;    // fp8 codes of h
-  float* hs;      // fp8 row scales of h
-  uint8_t* aq;    // fp8 codes of a
-  float* as;      // fp8 row scales of a
-};
-
-FfnBuffers carve_ffn(Carver& cv, int32_t w_dtype, int inter, int hidden, int64_t a_rows,
-                     int64_t rows, int n_mats) {
-  FfnPlan f = plan_ffn(w_dtype, rows, n_mats);
-  FfnBuffers b{};
-  b.sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.mtiles)));
-  const size_t hsz = w_dtype == MOE_BF16 ? 2 : 4;
-  b.h = cv.take<void>(size_t(rows) * inter * hsz);
-  if (w_dtype == MOE_FP8_E4M3) {
-    b.hq = cv.take<uint8_t>(size_t(rows) * inter);
-    b.hs = cv.take<float>(sizeof(float) * size_t(rows));
-    b.aq = cv.take<uint8_t>(size_t(a_rows) * hidden);
-    b.as = cv.take<float>(sizeof(float) * size_t(a_rows));
+void carve_mlp_buffers(Carver& cv, Mlp& m, int hidden) {
+  const size_t hsz = m.w_dtype == MOE_BF16 ? 2 : 4;
+  m.h = cv.take<void>(size_t(m.rows) * m.inter * hsz);
+  if (m.w_dtype == MOE_FP8_E4M3) {
+    m.hq = cv.take<uint8_t>(size_t(m.rows) * m.inter);
+    m.hs = cv.take<float>(sizeof(float) * size_t(m.rows));
+    m.aq = cv.take<uint8_t>(size_t(m.a_rows) * hidden);
+    m.as = cv.take<float>(sizeof(float) * size_t(m.a_rows));
   }
-  return b;
 }
 
-// Timing slots of one grouped MLP: quantise a, up GEMM, quantise h, down GEMM.
+GemmProblem up_problem(const Mlp& m, int hidden) {
+  GemmProblem p{};
+  const bool fp8 = m.w_dtype == MOE_FP8_E4M3;
+  p.a = fp8 ? static_cast<const void*>(m.aq) : m.a;
+  p.a_scale = fp8 ? m.as : nullptr;
+  p.row_index = m.row_index;
+  p.w = m.w_up;
+  p.w_scale = m.up_scale;
+  p.offsets = m.offsets;
+  p.out = m.h;
+  p.a_rows = m.a_rows;
+  p.rows = m.rows;
+  p.n = m.inter;
+  p.k = hidden;
+  p.index_div = m.index_div;
+  p.out_bf16 = m.w_dtype == MOE_BF16;
+  return p;
+}
+
+GemmProblem down_problem(const Mlp& m, int hidden) {
+  GemmProblem p{};
+  const bool fp8 = m.w_dtype == MOE_FP8_E4M3;
+  p.a = fp8 ? static_cast<const void*>(m.hq) : m.h;
+  p.a_scale = fp8 ? m.hs : nullptr;
+  p.row_index = nullptr;
+  p.w = m.w_down;
+  p.w_scale = m.down_scale;
+  p.offsets = m.offsets;
+  p.out = m.out;
+  p.a_rows = m.rows;
+  p.rows = m.rows;
+  p.n = hidden;
+  p.k = m.inter;
+  p.index_div = 1;
+  p.out_bf16 = 0;
+  return p;
+}
+
 struct FfnTiming {
   Timing qa, up, qh, down;
 };
 
-moe_status run_ffn(const moe_config& c, int n_mats, int inter, int32_t w_dtype, int64_t a_rows,
-                   const void* a, int64_t rows, const int32_t* offsets, const int32_t* row_index,
-                   int index_div, const void* w_up, const float* up_scale, const void* w_down,
-                   const float* down_scale, float* out, const FfnBuffers& b, hipStream_t s,
-                   const FfnTiming& tm = FfnTiming{}) {
-  if (rows == 0) return MOE_OK;
-  const FfnPlan f = plan_ffn(w_dtype, rows, n_mats);
-  hipError_t e;
-  ScheduleArgs sp{offsets, b.sched, rows, n_mats, f.shape.bm, static_cast<int>(f.mtiles)};
-  if ((e = launch_schedule(sp, s)) != hipSuccess) return MOE_ERR_HIP;
-  const int kind = kind_of(w_dtype);
-  const void* a_op = a;
-  const float* a_sc = nullptr;
-  if (kind == K_FP8) {
-    QuantArgs q{a, b.aq, b.as, a_rows, c.hidden, 1, nullptr};
-    if ((e = launch_quant(q, s, tm.qa)) != hipSuccess) return MOE_ERR_HIP;
-    a_op = b.aq;
-    a_sc = b.as;
+// Runs `m` (and `extra`, a single-group family of the same weight type, in
+// the same launches).  `sched` holds the schedule already when `have_sched`.
+moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, bool have_sched,
+                    hipStream_t s, const FfnTiming& tm) {
+  const int64_t extra_rows = extra ? extra->rows : 0;
+  if (m.rows == 0 && extra_rows == 0) return MOE_OK;
+  const FfnPlan f = plan_ffn(m.w_dtype, m.rows, m.n_mats, extra_rows);
+  if (!have_sched) {
+    ScheduleArgs sp{m.offsets, m.rows, m.n_mats,
+                    ScheduleSpec{sched, extra_rows, f.shape.bm, static_cast<int>(f.mtiles)}};
+    if (launch_schedule(sp, s) != hipSuccess) return MOE_ERR_HIP;
   }
-  GemmArgs up{};
-  up.a = a_op;
-  up.a_scale = a_sc;
-  up.row_index = row_index;
-  up.w = w_up;
-  up.w_scale = up_scale;
-  up.offsets = offsets;
-  up.sched = b.sched;
-  up.out = b.h;
-  up.a_rows = a_rows;
-  up.rows = rows;
-  up.n = inter;
-  up.k = c.hidden;
-  up.index_div = index_div;
-  up.n_tiles = (inter + f.shape.bn - 1) / f.shape.bn;
-  up.out_bf16 = w_dtype == MOE_BF16;
-  if ((e = launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s, tm.up)) != hipSuccess)
-    return MOE_ERR_HIP;
-  const void* h_op = b.h;
-  const float* h_sc = nullptr;
+  const int kind = kind_of(m.w_dtype);
   if (kind == K_FP8) {
-    QuantArgs q{b.h, b.hq, b.hs, rows, inter, 0, nullptr};
-    if ((e = launch_quant(q, s, tm.qh)) != hipSuccess) return MOE_ERR_HIP;
-    h_op = b.hq;
-    h_sc = b.hs;
+    QuantArgs q{m.a, m.aq, m.as, m.a_rows, hidden, 1};
+    if (launch_quant(q, s, tm.qa) != hipSuccess) return MOE_ERR_HIP;
+  }
+  const int bn = f.shape.bn;
+  GemmArgs up{};
+  up.prob[0] = up_problem(m, hidden);
+  if (extra) up.prob[1] = up_problem(*extra, hidden);
+  up.sched = sched;
+  up.n_groups = m.n_mats;
+  up.n_tiles = (std::max(m.inter, extra ? extra->inter : 0) + bn - 1) / bn;
+  if (launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s, tm.up) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (kind == K_FP8) {
+    QuantArgs q{m.h, m.hq, m.hs, m.rows, m.inter, 0};
+    if (launch_quant(q, s, tm.qh) != hipSuccess) return MOE_ERR_HIP;
   }
   GemmArgs dn{};
-  dn.a = h_op;
-  dn.a_scale = h_sc;
-  dn.row_index = nullptr;
-  dn.w = w_down;
-  dn.w_scale = down_scale;
-  dn.offsets = offsets;
-  dn.sched = b.sched;
-  dn.out = out;
-  dn.a_rows = rows;
-  dn.rows = rows;
-  dn.n = c.hidden;
-  dn.k = inter;
-  dn.index_div = 1;
-  dn.n_tiles = (c.hidden + f.shape.bn - 1) / f.shape.bn;
-  dn.out_bf16 = 0;
-  if ((e = launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down)) != hipSuccess)
+  dn.prob[0] = down_problem(m, hidden);
+  if (extra) dn.prob[1] = down_problem(*extra, hidden);
+  dn.sched = sched;
+  dn.n_groups = m.n_mats;
+  dn.n_tiles = (hidden + bn - 1) / bn;
+  if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
 
 // ---------------------------------------------------------- forward layout
 
-struct FwdBuffers {
-  int32_t* block_counts;
-  int32_t* topk_idx;
-  float* topk_w;
-  int32_t* counts;
-  int32_t* offsets;
-  int32_t* sorted_slot;
-  int32_t* slot_pos;
-  float* y_perm;
-  float* shared_out;
-  FfnBuffers routed;
-  FfnBuffers shared;
+struct Forward {
+  int64_t T = 0, S = 0;
+  bool fused_shared = false;
+  float* logits = nullptr;  // router logits (many tokens)
+  int32_t* block_counts = nullptr;
+  int32_t* topk_idx = nullptr;
+  float* topk_w = nullptr;
+  int32_t* counts = nullptr;
+  int32_t* offsets = nullptr;
+  int32_t* sorted_slot = nullptr;
+  int32_t* slot_pos = nullptr;
+  int32_t* sched = nullptr;
+  int32_t* shared_sched = nullptr;
+  FfnPlan plan{};
+  Mlp routed, shared;
 };
 
 int permute_chunks(int64_t slots) {
-  return static_cast<int>((slots + PERMUTE_CHUNK - 1) / PERMUTE_CHUNK);
+  return static_cast<int>((slots + PM_CHUNK - 1) / PM_CHUNK);
 }
 
-FwdBuffers carve_forward(Carver& cv, const moe_config& c, int64_t T) {
-  FwdBuffers b{};
-  const int64_t S = T * c.top_k;
-  b.block_counts = cv.take<int32_t>(sizeof(int32_t) * size_t(permute_chunks(S)) * c.n_experts);
-  b.topk_idx = cv.take<int32_t>(sizeof(int32_t) * size_t(S));
-  b.topk_w = cv.take<float>(sizeof(float) * size_t(S));
-  b.counts = cv.take<int32_t>(sizeof(int32_t) * c.n_experts);
-  b.offsets = cv.take<int32_t>(sizeof(int32_t) * (c.n_experts + 1));
-  b.sorted_slot = cv.take<int32_t>(sizeof(int32_t) * size_t(S));
-  b.slot_pos = cv.take<int32_t>(sizeof(int32_t) * size_t(S));
-  b.y_perm = cv.take<float>(sizeof(float) * size_t(S) * c.hidden);
-  b.routed = carve_ffn(cv, c.expert_dtype, c.inter, c.hidden, T, S, c.n_experts);
+// Router path for T tokens given room for the logits (all give the same bits).
+int route_mode(int64_t T) {
+  if (T <= ROUTE_WAVES_MAX_TOKENS) return ROUTE_WAVES;
+  if (T > ROUTE_DIRECT_MAX_TOKENS) return ROUTE_GEMM;
+  return ROUTE_ONE_KERNEL;
+}
+
+size_t route_logit_bytes(const moe_config& c, int64_t T) {
+  return sizeof(float) * size_t(T) * c.n_experts;
+}
+
+Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
+  Forward f;
+  f.T = T;
+  f.S = T * c.top_k;
+  f.fused_shared = c.shared_inter > 0 && c.expert_dtype == c.act_dtype;
+  if (route_mode(T) != ROUTE_ONE_KERNEL) f.logits = cv.take<float>(route_logit_bytes(c, T));
+  f.block_counts = cv.take<int32_t>(sizeof(int32_t) * size_t(permute_chunks(f.S)) * c.n_experts);
+  f.topk_idx = cv.take<int32_t>(sizeof(int32_t) * size_t(f.S));
+  f.topk_w = cv.take<float>(sizeof(float) * size_t(f.S));
+  f.counts = cv.take<int32_t>(sizeof(int32_t) * c.n_experts);
+  f.offsets = cv.take<int32_t>(sizeof(int32_t) * (c.n_experts + 1));
+  f.sorted_slot = cv.take<int32_t>(sizeof(int32_t) * size_t(f.S));
+  f.slot_pos = cv.take<int32_t>(sizeof(int32_t) * size_t(f.S));
+
+  Mlp& r = f.routed;
+  r.n_mats = c.n_experts;
+  r.inter = c.inter;
+  r.w_dtype = c.expert_dtype;
+  r.a_rows = T;
+  r.rows = f.S;
+  r.offsets = f.offsets;
+  r.row_index = f.sorted_slot;
+  r.index_div = c.top_k;
+  r.out = cv.take<float>(sizeof(float) * size_t(f.S) * c.hidden);  // y_perm
+  carve_mlp_buffers(cv, r, c.hidden);
   if (c.shared_inter > 0) {
-    b.shared_out = cv.take<float>(sizeof(float) * size_t(T) * c.hidden);
-    b.shared = carve_ffn(cv, c.act_dtype, c.shared_inter, c.hidden, T, T, 1);
+    Mlp& sh = f.shared;
+    sh.n_mats = 1;
+    sh.inter = c.shared_inter;
+    sh.w_dtype = c.act_dtype;
+    sh.a_rows = T;
+    sh.rows = T;
+    sh.out = cv.take<float>(sizeof(float) * size_t(T) * c.hidden);
+    carve_mlp_buffers(cv, sh, c.hidden);
   }
-  return b;
+  f.plan = plan_ffn(r.w_dtype, r.rows, r.n_mats, f.fused_shared ? T : 0);
+  f.sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.plan.mtiles)));
+  if (c.shared_inter > 0 && !f.fused_shared) {
+    const FfnPlan ps = plan_ffn(c.act_dtype, T, 1, 0);
+    f.shared_sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(ps.mtiles)));
+  }
+  return f;
 }
 
-moe_status do_route(const moe_config& c, int64_t T, const void* x, const void* w_gate,
-                    const float* e_bias, int32_t* topk_idx, float* topk_w, hipStream_t s,
-                    Timing t = {}) {
-  RouteArgs p{x, w_gate, e_bias, topk_idx, topk_w, T, c.hidden, c.n_experts, c.n_group,
-              c.topk_group, c.top_k, c.norm_topk_prob, c.routed_scaling_factor};
-  return hip_status(launch_route(p, kind_of(c.act_dtype), s, t));
+RouteArgs route_args(const moe_config& c, int64_t T, const void* x, const void* w_gate,
+                     const float* e_bias, int32_t* topk_idx, float* topk_w, float* logits) {
+  return RouteArgs{x, w_gate, e_bias, topk_idx, topk_w, logits, T, c.hidden, c.n_experts,
+                   c.n_group, c.topk_group, c.top_k, c.norm_topk_prob, c.routed_scaling_factor};
 }
 
 moe_status do_permute(const moe_config& c, int64_t T, const int32_t* topk_idx, int32_t* counts,
                       int32_t* offsets, int32_t* sorted_slot, int32_t* slot_pos,
-                      int32_t* block_counts, hipStream_t s, Timing t = {}) {
+                      int32_t* block_counts, ScheduleSpec spec, hipStream_t s, Timing t = {}) {
   const int64_t S = T * c.top_k;
   PermuteArgs p{topk_idx, counts, offsets, sorted_slot, slot_pos, block_counts, S,
-                PERMUTE_CHUNK, permute_chunks(S), c.n_experts};
+                permute_chunks(S), c.n_experts, spec};
   return hip_status(launch_permute(p, s, t));
 }
 
-Timing slot(void* const* ev, int i) {
-  if (!ev) return Timing{};
-  return Timing{static_cast<hipEvent_t>(ev[2 * i]), static_cast<hipEvent_t>(ev[2 * i + 1])};
+Mlp standalone_mlp(int32_t n_mats, int32_t inter, int32_t w_dtype, int64_t a_rows,
+                   const void* a, int64_t rows, const int32_t* row_offsets,
+                   const int32_t* row_index, int32_t index_div) {
+  Mlp m;
+  m.n_mats = n_mats;
+  m.inter = inter;
+  m.w_dtype = w_dtype;
+  m.a_rows = a_rows;
+  m.a = a;
+  m.rows = rows;
+  m.offsets = row_offsets;
+  m.row_index = row_index;
+  m.index_div = index_div;
+  return m;
+}
+
+size_t carve_standalone(Carver& cv, Mlp& m, int hidden, int32_t** sched) {
+  const FfnPlan f = plan_ffn(m.w_dtype, m.rows, m.n_mats, 0);
+  *sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.mtiles)));
+  carve_mlp_buffers(cv, m, hidden);
+  return cv.used;
 }
 
 }  // namespace
@@ -277,8 +371,6 @@ moe_status moe_workspace_size(const moe_config* cfg, int64_t tokens, size_t* byt
 moe_status moe_route(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
                      const float* e_bias, int32_t* topk_idx, float* topk_w, void* workspace,
                      size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
@@ -286,8 +378,16 @@ moe_status moe_route(const moe_config* cfg, int64_t tokens, const void* x, const
   const void* ptrs[] = {x, w_gate, e_bias, topk_idx, topk_w};
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
-  return do_route(*cfg, tokens, x, w_gate, e_bias, topk_idx, topk_w,
-                  static_cast<hipStream_t>(stream));
+  // every router path gives the same bits; all but one need room for the logits
+  int mode = route_mode(tokens);
+  float* logits = nullptr;
+  if (mode != ROUTE_ONE_KERNEL && workspace && aligned16(workspace) &&
+      workspace_bytes >= route_logit_bytes(*cfg, tokens))
+    logits = static_cast<float*>(workspace);
+  if (!logits) mode = ROUTE_ONE_KERNEL;
+  const RouteArgs ra = route_args(*cfg, tokens, x, w_gate, e_bias, topk_idx, topk_w, logits);
+  return hip_status(launch_route(ra, kind_of(cfg->act_dtype), mode,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_permute(const moe_config* cfg, int64_t tokens, const int32_t* topk_idx,
@@ -309,12 +409,13 @@ moe_status moe_permute(const moe_config* cfg, int64_t tokens, const int32_t* top
     return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = do_permute(*cfg, tokens, topk_idx, expert_counts, expert_offsets, sorted_slot, slot_pos,
-                  static_cast<int32_t*>(workspace), s);
+                  static_cast<int32_t*>(workspace), ScheduleSpec{}, s);
   if (st != MOE_OK || !x) return st;
   GatherArgs g{x, x_perm, sorted_slot, S, static_cast<int>(cfg->hidden * esize(cfg->act_dtype)),
                cfg->top_k};
   return hip_status(launch_gather(g, s));
 }
+
 
 moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, int32_t inter,
                                          int32_t w_dtype, int64_t a_rows, int64_t rows,
@@ -324,8 +425,9 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
   if (!bytes || n_mats < 1 || inter <= 0 || a_rows < 0 || rows < 0) return MOE_ERR_INVALID_ARG;
   if (w_dtype < 0 || w_dtype > 2) return MOE_ERR_INVALID_ARG;
   Carver cv(nullptr);
-  carve_ffn(cv, w_dtype, inter, cfg->hidden, a_rows, rows, n_mats);
-  *bytes = cv.used;
+  Mlp m = standalone_mlp(n_mats, inter, w_dtype, a_rows, nullptr, rows, nullptr, nullptr, 1);
+  int32_t* sched;
+  *bytes = carve_standalone(cv, m, cfg->hidden, &sched);
   return MOE_OK;
 }
 
@@ -357,15 +459,22 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, 
     if (!w_up_scale || !w_down_scale || !aligned16(w_up_scale) || !aligned16(w_down_scale))
       return MOE_ERR_INVALID_ARG;
   }
+  Mlp m = standalone_mlp(n_mats, inter, w_dtype, a_rows, a, rows, row_offsets, row_index,
+                         index_div);
+  m.w_up = w_up;
+  m.up_scale = w_up_scale;
+  m.w_down = w_down;
+  m.down_scale = w_down_scale;
+  m.out = out;
   Carver measure(nullptr);
-  carve_ffn(measure, w_dtype, inter, cfg->hidden, a_rows, rows, n_mats);
-  if (!workspace || workspace_bytes < measure.used || !aligned16(workspace))
-    return MOE_ERR_WORKSPACE;
+  int32_t* sched;
+  Mlp probe = m;
+  const size_t need = carve_standalone(measure, probe, cfg->hidden, &sched);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
   Carver cv(workspace);
-  FfnBuffers b = carve_ffn(cv, w_dtype, inter, cfg->hidden, a_rows, rows, n_mats);
-  return run_ffn(*cfg, n_mats, inter, w_dtype, a_rows, a, rows, row_offsets, row_index, index_div,
-                 w_up, w_up_scale, w_down, w_down_scale, out, b,
-                 static_cast<hipStream_t>(stream));
+  carve_standalone(cv, m, cfg->hidden, &sched);
+  return run_mlps(cfg->hidden, m, nullptr, sched, false, static_cast<hipStream_t>(stream),
+                  FfnTiming{});
 }
 
 moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slot_pos,
@@ -411,31 +520,40 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
   if (!workspace || workspace_bytes < measure.used || !aligned16(workspace))
     return MOE_ERR_WORKSPACE;
   Carver cv(workspace);
-  FwdBuffers b = carve_forward(cv, c, tokens);
+  Forward f = carve_forward(cv, c, tokens);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* idx = topk_idx ? topk_idx : b.topk_idx;
-  float* wts = topk_w ? topk_w : b.topk_w;
-  int32_t* cnt = expert_counts ? expert_counts : b.counts;
-  const int64_t S = tokens * c.top_k;
+  int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
+  float* wts = topk_w ? topk_w : f.topk_w;
+  int32_t* cnt = expert_counts ? expert_counts : f.counts;
+  f.routed.a = x;
+  f.routed.w_up = w_up;
+  f.routed.up_scale = w_up_scale;
+  f.routed.w_down = w_down;
+  f.routed.down_scale = w_down_scale;
+  f.shared.a = x;
+  f.shared.w_up = ws_up;
+  f.shared.w_down = ws_down;
 
-  if ((st = do_route(c, tokens, x, w_gate, e_bias, idx, wts, s, slot(ev, MOE_T_ROUTE))) != MOE_OK)
-    return st;
-  if ((st = do_permute(c, tokens, idx, cnt, b.offsets, b.sorted_slot, b.slot_pos, b.block_counts,
-                       s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
+  const RouteArgs ra = route_args(c, tokens, x, w_gate, e_bias, idx, wts, f.logits);
+  if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  const ScheduleSpec spec{f.sched, f.fused_shared ? tokens : 0, f.plan.shape.bm,
+                          static_cast<int>(f.plan.mtiles)};
+  if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
+                       f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
     return st;
   FfnTiming rt{slot(ev, MOE_T_QUANT_X), slot(ev, MOE_T_ROUTED_UP), slot(ev, MOE_T_QUANT_H),
                slot(ev, MOE_T_ROUTED_DOWN)};
-  if ((st = run_ffn(c, c.n_experts, c.inter, c.expert_dtype, tokens, x, S, b.offsets,
-                    b.sorted_slot, c.top_k, w_up, w_up_scale, w_down, w_down_scale, b.y_perm,
-                    b.routed, s, rt)) != MOE_OK)
+  if ((st = run_mlps(c.hidden, f.routed, f.fused_shared ? &f.shared : nullptr, f.sched, true, s,
+                     rt)) != MOE_OK)
     return st;
-  if (c.shared_inter > 0) {
+  if (c.shared_inter > 0 && !f.fused_shared) {
     FfnTiming sh{Timing{}, slot(ev, MOE_T_SHARED_UP), Timing{}, slot(ev, MOE_T_SHARED_DOWN)};
-    if ((st = run_ffn(c, 1, c.shared_inter, c.act_dtype, tokens, x, tokens, nullptr, nullptr, 1,
-                      ws_up, nullptr, ws_down, nullptr, b.shared_out, b.shared, s, sh)) != MOE_OK)
+    if ((st = run_mlps(c.hidden, f.shared, nullptr, f.shared_sched, false, s, sh)) != MOE_OK)
       return st;
   }
-  CombineArgs p{b.slot_pos, wts, b.y_perm, c.shared_inter > 0 ? b.shared_out : nullptr, y,
+  CombineArgs p{f.slot_pos, wts, f.routed.out, c.shared_inter > 0 ? f.shared.out : nullptr, y,
                 tokens, c.hidden, c.top_k};
   return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_COMBINE)));
 }

@@ -29,18 +29,39 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key) {
   return m;
 }
 
-// Place the slots [s_begin, s_end) in order.  run[e] holds the next free
-// position of expert e and is advanced; wc is a zeroed [PM_WAVES][E] scratch.
-__device__ void place_chunk(const int32_t* __restrict__ idx, int64_t s_begin, int64_t s_end,
-                            int E, int32_t* run, int32_t* wc, int32_t* __restrict__ sorted_slot,
+// Copies the expert ids of slots [s0, s0 + n), n <= PM_CHUNK, into LDS.  All
+// loads are issued before the first store, so the chunk costs one memory
+// round trip.  Ids outside [0, E) are clamped so every later write stays
+// inside its array.  Ends with a barrier.
+__device__ void stage_ids(const int32_t* __restrict__ idx, int64_t s0, int n, int E,
+                          int32_t* ids) {
+  constexpr int PER = PM_CHUNK / PM_THREADS;
+  int32_t v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = threadIdx.x + i * PM_THREADS;
+    v[i] = q < n ? idx[s0 + q] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int q = threadIdx.x + i * PM_THREADS;
+    if (q < n) ids[q] = min(max(v[i], 0), E - 1);
+  }
+  __syncthreads();
+}
+
+// Place the slots [s_begin, s_begin + n) in order; ids[i] is the expert of
+// slot s_begin + i.  run[e] holds the next free position of expert e and is
+// advanced; wc is a zeroed [PM_WAVES][E] scratch.
+__device__ void place_chunk(const int32_t* ids, int64_t s_begin, int n, int E, int32_t* run,
+                            int32_t* wc, int32_t* __restrict__ sorted_slot,
                             int32_t* __restrict__ slot_pos) {
   const int wave = threadIdx.x / WAVE;
-  const int lane = lane_id();
-  for (int64_t r0 = s_begin; r0 < s_end; r0 += PM_THREADS) {
-    const int64_t s = r0 + threadIdx.x;
-    const bool valid = s < s_end;
-    // ids outside [0, E) are clamped so that every write stays inside the arrays
-    const int e = valid ? min(max(idx[s], 0), E - 1) : 0;
+  for (int r0 = 0; r0 < n; r0 += PM_THREADS) {
+    const int i = r0 + threadIdx.x;
+    const bool valid = i < n;
+    const int64_t s = s_begin + i;
+    const int e = valid ? ids[i] : 0;
     const uint32_t key = valid ? (uint32_t(e) | 0x200u) : 0u;
     const uint64_t m = match_key(key);
     const int rank = __popcll(m & lanemask_lt());
@@ -65,7 +86,6 @@ __device__ void place_chunk(const int32_t* __restrict__ idx, int64_t s_begin, in
       slot_pos[s] = pos;
     }
     __syncthreads();
-    (void)lane;
   }
 }
 
@@ -103,17 +123,67 @@ __device__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* tmp) {
   return total;
 }
 
-// Small problems (all slots in one workgroup): histogram, scan, placement.
+// M-tile schedule of a grouped GEMM (layout in internal.hpp): group g covers
+// the rows range(g) = [a, b); tiles of `bm` rows, groups in order, then the
+// optional extra group.  All threads must call; tiles/tmp are LDS scratch.
+template <typename Range>
+__device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp, int32_t* tiles,
+                              int32_t* tmp, int32_t* carry) {
+  if (threadIdx.x == 0) *carry = 0;
+  __syncthreads();
+  for (int g0 = 0; g0 < n_groups; g0 += 1024) {
+    const int n = min(1024, n_groups - g0);
+    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
+      int64_t a, b;
+      range(g0 + i, a, b);
+      tiles[i] = b > a ? static_cast<int32_t>((b - a + sp.bm - 1) / sp.bm) : 0;
+    }
+    __syncthreads();
+    const int32_t total = block_exclusive_scan(tiles, n, tmp);
+    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
+      int64_t a, b;
+      range(g0 + i, a, b);
+      int32_t at = *carry + tiles[i];
+      for (int64_t m = a; m < b; m += sp.bm, ++at) {
+        if (at < sp.max_tiles) {
+          sp.sched[2 + 2 * at] = g0 + i;
+          sp.sched[3 + 2 * at] = static_cast<int32_t>(m);
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *carry += total;
+    __syncthreads();
+  }
+  const int32_t extra =
+      sp.extra_rows > 0 ? static_cast<int32_t>((sp.extra_rows + sp.bm - 1) / sp.bm) : 0;
+  for (int j = threadIdx.x; j < extra; j += PM_THREADS) {
+    const int32_t at = *carry + j;
+    if (at < sp.max_tiles) {
+      sp.sched[2 + 2 * at] = n_groups;
+      sp.sched[3 + 2 * at] = j * sp.bm;
+    }
+  }
+  if (threadIdx.x == 0) sp.sched[0] = min(*carry + extra, sp.max_tiles);
+  __syncthreads();
+}
+
+// Small problems (all slots in one workgroup): histogram, scan, schedule,
+// placement.
 __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p) {
   __shared__ int32_t cnt[1024];
   __shared__ int32_t run[1024];
+  __shared__ int32_t tiles[1024];
   __shared__ int32_t wc[PM_WAVES * 256];
   __shared__ int32_t tmp[PM_THREADS];
+  __shared__ int32_t carry;
   const int E = p.n_experts;
+  __shared__ int32_t ids[PM_CHUNK];
+  const int n = static_cast<int>(p.slots);
   for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
   for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
-  __syncthreads();
-  for (int64_t s = threadIdx.x; s < p.slots; s += PM_THREADS) atomicAdd(&cnt[min(max(p.topk_idx[s], 0), E - 1)], 1);
+  stage_ids(p.topk_idx, 0, n, E, ids);
+  for (int i = threadIdx.x; i < n; i += PM_THREADS) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PM_THREADS) {
     run[e] = cnt[e];
@@ -122,38 +192,59 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p
   __syncthreads();
   block_exclusive_scan(run, E, tmp);
   for (int e = threadIdx.x; e < E; e += PM_THREADS) p.expert_offsets[e] = run[e];
-  if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
+  if (threadIdx.x == 0) p.expert_offsets[E] = n;
   __syncthreads();
-  place_chunk(p.topk_idx, 0, p.slots, E, run, wc, p.sorted_slot, p.slot_pos);
+  if (p.sched.sched)
+    emit_schedule(
+        [&](int g, int64_t& a, int64_t& b) {
+          a = run[g];
+          b = run[g] + cnt[g];
+        },
+        E, p.sched, tiles, tmp, &carry);
+  place_chunk(ids, 0, n, E, run, wc, p.sorted_slot, p.slot_pos);
 }
 
 // Large problems, pass 1: per-chunk expert histogram.
 __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(PermuteArgs p) {
   __shared__ int32_t cnt[256];
+  __shared__ int32_t ids[PM_CHUNK];
   const int E = p.n_experts;
   for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
-  __syncthreads();
-  const int64_t s0 = int64_t(blockIdx.x) * p.chunk;
-  const int64_t s1 = min<int64_t>(s0 + p.chunk, p.slots);
-  for (int64_t s = s0 + threadIdx.x; s < s1; s += PM_THREADS) atomicAdd(&cnt[min(max(p.topk_idx[s], 0), E - 1)], 1);
+  const int64_t s0 = int64_t(blockIdx.x) * PM_CHUNK;
+  const int n = static_cast<int>(min<int64_t>(PM_CHUNK, p.slots - s0));
+  stage_ids(p.topk_idx, s0, n, E, ids);
+  for (int i = threadIdx.x; i < n; i += PM_THREADS) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PM_THREADS) p.block_counts[blockIdx.x * E + e] = cnt[e];
 }
 
-// Pass 2 (one workgroup): per-expert totals, offsets, and each chunk's base.
+// Pass 2 (one workgroup): per-expert totals, offsets, each chunk's base, and
+// the GEMM schedule.
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p) {
   __shared__ int32_t off[1024];
+  __shared__ int32_t cnt[1024];
+  __shared__ int32_t tiles[1024];
   __shared__ int32_t tmp[PM_THREADS];
+  __shared__ int32_t carry;
   const int E = p.n_experts;
+  constexpr int B = 8;  // chunk counts loaded per batch
   for (int e = threadIdx.x; e < E; e += PM_THREADS) {
     int32_t total = 0;
-    for (int b = 0; b < p.n_chunks; ++b) {
-      int32_t v = p.block_counts[b * E + e];
-      p.block_counts[b * E + e] = total;  // becomes the chunk's base inside expert e
-      total += v;
+    for (int b0 = 0; b0 < p.n_chunks; b0 += B) {
+      int32_t v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) v[u] = b0 + u < p.n_chunks ? p.block_counts[(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        if (b0 + u < p.n_chunks) {
+          p.block_counts[(b0 + u) * E + e] = total;  // the chunk's base inside expert e
+          total += v[u];
+        }
+      }
     }
     p.expert_counts[e] = total;
     off[e] = total;
+    cnt[e] = total;
   }
   __syncthreads();
   block_exclusive_scan(off, E, tmp);
@@ -162,19 +253,27 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p)
     for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];
   }
   if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
+  if (p.sched.sched)
+    emit_schedule(
+        [&](int g, int64_t& a, int64_t& b) {
+          a = off[g];
+          b = off[g] + cnt[g];
+        },
+        E, p.sched, tiles, tmp, &carry);
 }
 
 // Pass 3: stable placement of each chunk from its base.
 __global__ __launch_bounds__(PM_THREADS) void permute_place_kernel(PermuteArgs p) {
   __shared__ int32_t run[256];
   __shared__ int32_t wc[PM_WAVES * 256];
+  __shared__ int32_t ids[PM_CHUNK];
   const int E = p.n_experts;
   for (int e = threadIdx.x; e < E; e += PM_THREADS) run[e] = p.block_counts[blockIdx.x * E + e];
   for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
-  __syncthreads();
-  const int64_t s0 = int64_t(blockIdx.x) * p.chunk;
-  const int64_t s1 = min<int64_t>(s0 + p.chunk, p.slots);
-  place_chunk(p.topk_idx, s0, s1, E, run, wc, p.sorted_slot, p.slot_pos);
+  const int64_t s0 = int64_t(blockIdx.x) * PM_CHUNK;
+  const int n = static_cast<int>(min<int64_t>(PM_CHUNK, p.slots - s0));
+  stage_ids(p.topk_idx, s0, n, E, ids);
+  place_chunk(ids, s0, n, E, run, wc, p.sorted_slot, p.slot_pos);
 }
 
 // x_perm[r] = x[sorted_slot[r] / k], 16 bytes per lane.
@@ -192,43 +291,18 @@ __global__ __launch_bounds__(PM_THREADS) void gather_rows_kernel(GatherArgs p) {
   }
 }
 
-// M-tile schedule of a grouped GEMM: entry i = (group, first row) of the i-th
-// tile of `bm` rows; tiles of one group are consecutive, groups in order.
-// sched[0] = number of tiles, entries from sched + 2.
+// Schedule of a grouped GEMM from group offsets in global memory.
 __global__ __launch_bounds__(PM_THREADS) void schedule_kernel(ScheduleArgs p) {
   __shared__ int32_t tiles[1024];
   __shared__ int32_t tmp[PM_THREADS];
   __shared__ int32_t carry;
-  if (threadIdx.x == 0) carry = 0;
-  for (int g0 = 0; g0 < p.n_groups; g0 += 1024) {
-    const int n = min(1024, p.n_groups - g0);
-    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
-      const int g = g0 + i;
-      // no offsets: a single group spans every row
-      const int64_t a = p.offsets ? min<int64_t>(max(p.offsets[g], 0), p.rows) : 0;
-      const int64_t b = p.offsets ? min<int64_t>(max(p.offsets[g + 1], 0), p.rows) : p.rows;
-      tiles[i] = b > a ? static_cast<int32_t>((b - a + p.bm - 1) / p.bm) : 0;
-    }
-    __syncthreads();
-    const int32_t total = block_exclusive_scan(tiles, n, tmp);
-    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
-      const int g = g0 + i;
-      // no offsets: a single group spans every row
-      const int64_t a = p.offsets ? min<int64_t>(max(p.offsets[g], 0), p.rows) : 0;
-      const int64_t b = p.offsets ? min<int64_t>(max(p.offsets[g + 1], 0), p.rows) : p.rows;
-      int32_t at = carry + tiles[i];
-      for (int64_t m = a; m < b; m += p.bm, ++at) {
-        if (at < p.max_tiles) {
-          p.sched[2 + 2 * at] = g;
-          p.sched[3 + 2 * at] = static_cast<int32_t>(m);
-        }
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) carry += total;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) p.sched[0] = min(carry, p.max_tiles);
+  emit_schedule(
+      [&](int g, int64_t& a, int64_t& b) {
+        // no offsets: a single group spans every row
+        a = p.offsets ? min<int64_t>(max(p.offsets[g], 0), p.rows) : 0;
+        b = p.offsets ? min<int64_t>(max(p.offsets[g + 1], 0), p.rows) : p.rows;
+      },
+      p.n_groups, p.spec, tiles, tmp, &carry);
 }
 
 // y[t] = sum_j w[t,j] * y_perm[slot_pos[t*k+j]] (+ shared[t]), fp32, rounded once.

@@ -1,4 +1,4 @@
-// route.hip -- router logits and grouped top-k selection, one kernel.
+// route.hip -- router logits and grouped top-k selection.
 //
 // Layer statement: baseRT issue "Requesting converter + runtime support for
 // the Nemotron-H architecture", section "Architecture (config.json)" (128
@@ -7,179 +7,152 @@
 // Nemotron-H / Nemotron-Cascade-2", discussion.  Sigmoid scoring, the top-2
 // group score and selection-only use of the bias are this library's reading.
 //
-// One workgroup (4 waves) owns 16 tokens.  Logits l[16][E] come from MFMA
-// (bf16 16x16x32, or four f32 16x16x4 steps) with both operands read straight
-// from global memory into registers: x rows and gate rows are K-contiguous,
-// so every lane loads 16 contiguous bytes and no LDS staging is needed.  Each
-// wave owns E/64 of the 16-expert column blocks.  The logits then go through
-// LDS to the selection phase, where each wave takes four tokens and does the
-// grouped top-k with wave-wide reductions.
-#include "internal.hpp"
+// Logits l = x Wg^T accumulate in fp32 on MFMA (bf16 16x16x32, or four f32
+// 16x16x4 steps per 64 bytes of K), one MFMA per K step in ascending K, the
+// same order the grouped GEMM kernels use.  Three ways to get them give the
+// same bits, so a token's routing does not depend on how many tokens share
+// the call:
+//   * route_logits_kernel (very few tokens): one wave per (16 tokens, 16
+//     experts) block, so the gate matrix streams through many compute units
+//     instead of one; logits go to the workspace, then route_select_kernel.
+//   * route_kernel (few tokens, or no workspace): one workgroup per 16 tokens
+//     computes all their logits and selects from LDS.
+//   * many tokens: the logits are one dense GEMM (gemm.hip) into the
+//     workspace, then route_select_kernel.
+// Operands go from global memory straight into MFMA registers (x rows and
+// gate rows are K-contiguous: 16 contiguous bytes per lane).
+#include "select.hpp"
 
 namespace moe {
 
 namespace {
 
-constexpr int RT_TOK = 16;   // tokens per workgroup
-constexpr int RT_MAXE = 256; // experts supported
-constexpr int RT_EPL = RT_MAXE / WAVE;
+constexpr int RT_TOK = 16;     // tokens per block
+constexpr int RT_WAVES = 8;    // waves of route_kernel
+constexpr int ROUTE_U = 8;     // K steps in flight per wave (route_kernel)
+constexpr int LOGIT_U = 21;    // K steps in flight per wave (route_logits_kernel)
+
+// Logits of 16 tokens x 16 experts: lane holds expert row, tokens 4*grp..+3.
+template <int KIND, int U>
+__device__ __forceinline__ f32x4_t logit_block(const char* xrow, const char* grow, int steps) {
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    i32x4_t a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < steps) {
+        a[u] = *reinterpret_cast<const i32x4_t*>(xrow + (s0 + u) * 64);
+        b[u] = *reinterpret_cast<const i32x4_t*>(grow + (s0 + u) * 64);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s0 + u < steps)
+        acc = KIND == K_F32 ? mfma_f32x4(a[u], b[u], acc) : mfma_bf16(a[u], b[u], acc);
+  }
+  return acc;
+}
 
 template <int KIND>
-__device__ __forceinline__ void router_logits(const RouteArgs& p, int64_t t0, float* lds_logit) {
+__global__ __launch_bounds__(RT_WAVES * WAVE) void route_kernel(RouteArgs p) {
+  __shared__ float lds_logit[RT_TOK * (RT_MAXE + 1)];
+  __shared__ SelScratch scr[RT_WAVES];
+  const int64_t t0 = int64_t(blockIdx.x) * RT_TOK;
   const int lane = lane_id();
   const int wave = threadIdx.x / WAVE;
   const int row = lane & 15;
   const int grp = lane >> 4;
+  const int row_bytes = p.hidden * (KIND == K_F32 ? 4 : 2);
   const int64_t t = min<int64_t>(t0 + row, p.tokens - 1);  // tail rows read the last token
-  const int d = p.hidden;
-  const int row_bytes = d * (KIND == K_F32 ? 4 : 2);
-  const char* xrow = static_cast<const char*>(p.x) + t * row_bytes;
-  const int nblk = p.n_experts / 16;
-  for (int nb = wave; nb < nblk; nb += 4) {
-    const char* grow = static_cast<const char*>(p.w_gate) + int64_t(nb * 16 + row) * row_bytes;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    // 64-byte K step per MFMA group; unrolled by 4 to keep loads in flight
-    const int steps = row_bytes / 64;
-    int s = 0;
-    for (; s + 4 <= steps; s += 4) {
-      i32x4_t a[4], b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = *reinterpret_cast<const i32x4_t*>(xrow + (s + u) * 64 + grp * 16);
-        b[u] = *reinterpret_cast<const i32x4_t*>(grow + (s + u) * 64 + grp * 16);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc = KIND == K_F32 ? mfma_f32x4(a[u], b[u], acc) : mfma_bf16(a[u], b[u], acc);
-    }
-    for (; s < steps; ++s) {
-      i32x4_t a = *reinterpret_cast<const i32x4_t*>(xrow + s * 64 + grp * 16);
-      i32x4_t b = *reinterpret_cast<const i32x4_t*>(grow + s * 64 + grp * 16);
-      acc = KIND == K_F32 ? mfma_f32x4(a, b, acc) : mfma_bf16(a, b, acc);
-    }
-    // lane holds expert nb*16 + row, tokens 4*grp .. 4*grp+3
+  const char* xrow = static_cast<const char*>(p.x) + t * row_bytes + grp * 16;
+  for (int nb = wave; nb < p.n_experts / 16; nb += RT_WAVES) {
+    const char* grow =
+        static_cast<const char*>(p.w_gate) + int64_t(nb * 16 + row) * row_bytes + grp * 16;
+    const f32x4_t acc = logit_block<KIND, ROUTE_U>(xrow, grow, row_bytes / 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds_logit[(4 * grp + i) * (RT_MAXE + 1) + nb * 16 + row] = acc[i];
   }
-}
-
-__device__ void select_one(const RouteArgs& p, const float* logit, int64_t t, float* sc,
-                           float* gsc) {
-  const int lane = lane_id();
-  const int E = p.n_experts, G = p.n_group, Eg = E / G;
-  float s[RT_EPL], c[RT_EPL];
-  // expert e = lane + 64 * j
-#pragma unroll
-  for (int j = 0; j < RT_EPL; ++j) {
-    const int e = lane + WAVE * j;
-    if (e < E) {
-      float l = logit[e];
-      s[j] = 1.0f / (1.0f + expf(-l));
-      c[j] = s[j] + p.e_bias[e];
-      sc[e] = c[j];
-    } else {
-      s[j] = 0.f;
-      c[j] = -INFINITY;
-    }
-  }
-  wave_lds_sync();
-  // group scores: lane g sums the two largest c of its group
-  float gs = -INFINITY;
-  if (lane < G) {
-    float b1 = -INFINITY, b2 = -INFINITY;
-    for (int e = lane * Eg; e < (lane + 1) * Eg; ++e) {
-      float v = sc[e];
-      if (v > b1) {
-        b2 = b1;
-        b1 = v;
-      } else if (v > b2) {
-        b2 = v;
-      }
-    }
-    gs = Eg == 1 ? b1 : b1 + b2;
-  }
-  // keep topk_group groups
-  uint64_t gmask = 0;
-  for (int r = 0; r < p.topk_group; ++r) {
-    float v = ((gmask >> lane) & 1) || lane >= G ? -INFINITY : gs;
-    int i = lane < G && !((gmask >> lane) & 1) ? lane : 0x7FFFFFFF;
-    wave_argmax(v, i);
-    if (i < G) gmask |= uint64_t(1) << i;
-  }
-  // keep top_k experts inside the kept groups
-  bool sel[RT_EPL];
-  bool elig[RT_EPL];
-#pragma unroll
-  for (int j = 0; j < RT_EPL; ++j) {
-    const int e = lane + WAVE * j;
-    sel[j] = false;
-    elig[j] = e < E && ((gmask >> (e / Eg)) & 1);
-  }
-  for (int r = 0; r < p.top_k; ++r) {
-    float v = -INFINITY;
-    int i = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < RT_EPL; ++j) {
-      const int e = lane + WAVE * j;
-      if (elig[j] && !sel[j] && (c[j] > v || (c[j] == v && e < i))) {
-        v = c[j];
-        i = e;
-      }
-    }
-    wave_argmax(v, i);
-#pragma unroll
-    for (int j = 0; j < RT_EPL; ++j)
-      if (lane + WAVE * j == i) sel[j] = true;
-  }
-  // ascending expert ids: rank = selected experts with a smaller id
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < RT_EPL; ++j) {
-    uint64_t bj = ballot(sel[j]);
-    if (sel[j]) {
-      int rank = base + __popcll(bj & lanemask_lt());
-      gsc[rank] = s[j];
-      p.topk_idx[t * p.top_k + rank] = lane + WAVE * j;
-    }
-    base += __popcll(bj);
-  }
-  wave_lds_sync();
-  if (lane < p.top_k) {
-    float w = gsc[lane];
-    if (p.norm_topk_prob) {
-      float denom = 0.f;
-      for (int r = 0; r < p.top_k; ++r) denom += gsc[r];
-      w = p.scale * (w / denom);
-    } else {
-      w = p.scale * w;
-    }
-    p.topk_w[t * p.top_k + lane] = w;
-  }
-  wave_lds_sync();
-}
-
-template <int KIND>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs p) {
-  __shared__ float lds_logit[RT_TOK * (RT_MAXE + 1)];
-  __shared__ float lds_c[4][RT_MAXE];
-  __shared__ float lds_s[4][64];
-  const int64_t t0 = int64_t(blockIdx.x) * RT_TOK;
-  router_logits<KIND>(p, t0, lds_logit);
   __syncthreads();
-  const int wave = threadIdx.x / WAVE;
-  for (int i = wave; i < RT_TOK; i += 4) {
-    const int64_t t = t0 + i;
-    if (t >= p.tokens) break;
-    select_one(p, lds_logit + i * (RT_MAXE + 1), t, lds_c[wave], lds_s[wave]);
+  for (int i = wave; i < RT_TOK; i += RT_WAVES) {
+    const int64_t tt = t0 + i;
+    if (tt >= p.tokens) break;
+    select_one(p, lds_logit + i * (RT_MAXE + 1), tt, scr[wave], p.e_bias);
   }
+}
+
+// One wave per (token block, expert block): logits [tokens, E] to the workspace.
+template <int KIND>
+__global__ __launch_bounds__(WAVE) void route_logits_kernel(RouteArgs p) {
+  const int nblk = p.n_experts / 16;
+  const int nb = blockIdx.x % nblk;
+  const int64_t t0 = int64_t(blockIdx.x / nblk) * RT_TOK;
+  const int lane = lane_id();
+  const int row = lane & 15;
+  const int grp = lane >> 4;
+  const int row_bytes = p.hidden * (KIND == K_F32 ? 4 : 2);
+  const int64_t t = min<int64_t>(t0 + row, p.tokens - 1);
+  const char* xrow = static_cast<const char*>(p.x) + t * row_bytes + grp * 16;
+  const char* grow =
+      static_cast<const char*>(p.w_gate) + int64_t(nb * 16 + row) * row_bytes + grp * 16;
+  const f32x4_t acc = logit_block<KIND, LOGIT_U>(xrow, grow, row_bytes / 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t tok = t0 + 4 * grp + i;
+    if (tok < p.tokens) p.logits[tok * p.n_experts + nb * 16 + row] = acc[i];
+  }
+}
+
+// Selection from logits [tokens, E] in global memory, one wave per token.
+__global__ __launch_bounds__(256) void route_select_kernel(RouteArgs p) {
+  __shared__ float lds_l[4][RT_MAXE];
+  __shared__ SelScratch scr[4];
+  const int wave = threadIdx.x / WAVE;
+  const int lane = lane_id();
+  const int64_t t = int64_t(blockIdx.x) * 4 + wave;
+  if (t >= p.tokens) return;
+  for (int e = lane; e < p.n_experts; e += WAVE) lds_l[wave][e] = p.logits[t * p.n_experts + e];
+  wave_lds_sync();
+  select_one(p, lds_l[wave], t, scr[wave], p.e_bias);
 }
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& p, int kind, hipStream_t stream, Timing t) {
-  dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK));
-  if (kind == K_F32) return launch_k(route_kernel<K_F32>, grid, dim3(256), stream, t, p);
-  return launch_k(route_kernel<K_BF16>, grid, dim3(256), stream, t, p);
+hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stream, Timing t) {
+  const Timing first{t.start, nullptr};
+  hipError_t e = hipSuccess;
+  if (mode == ROUTE_ONE_KERNEL) {
+    dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK));
+    dim3 block(RT_WAVES * WAVE);
+    if (kind == K_F32) return launch_k(route_kernel<K_F32>, grid, block, stream, t, p);
+    return launch_k(route_kernel<K_BF16>, grid, block, stream, t, p);
+  }
+  if (mode == ROUTE_WAVES) {
+    dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK * (p.n_experts / 16)));
+    if (kind == K_F32)
+      e = launch_k(route_logits_kernel<K_F32>, grid, dim3(WAVE), stream, first, p);
+    else
+      e = launch_k(route_logits_kernel<K_BF16>, grid, dim3(WAVE), stream, first, p);
+  } else {  // ROUTE_GEMM: the logits as a dense GEMM
+    GemmArgs g{};
+    GemmProblem& q = g.prob[0];
+    q.a = p.x;
+    q.w = p.w_gate;
+    q.out = p.logits;
+    q.a_rows = p.tokens;
+    q.rows = p.tokens;
+    q.n = p.n_experts;
+    q.k = p.hidden;
+    q.index_div = 1;
+    g.sched = nullptr;
+    g.n_groups = 1;
+    const GemmShape shape{128, 128};
+    g.n_tiles = (p.n_experts + shape.bn - 1) / shape.bn;
+    const int64_t mtiles = (p.tokens + shape.bm - 1) / shape.bm;
+    e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, stream, first);
+  }
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>((p.tokens + 3) / 4));
+  return launch_k(route_select_kernel, grid, dim3(256), stream, Timing{nullptr, t.stop}, p);
 }
 
 }  // namespace moe

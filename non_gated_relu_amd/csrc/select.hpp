@@ -1,0 +1,169 @@
+// select.hpp -- grouped top-k selection of one token, one wave.
+//
+// Rule (baseRT issue "Requesting converter + runtime support for the
+// Nemotron-H architecture", section "Architecture (config.json)": grouped
+// top-k with n_groups and topk_group, norm_topk_prob, routed_scaling_factor;
+// sigmoid scores, selection-only correction bias, top-2 group score and
+// lowest-index tie break are this library's reading):
+//   s = sigmoid(l), c = s + b; group score = sum of the two largest c of the
+//   group; keep topk_group groups, then the top_k experts of largest c in
+//   them; w_j = scale * s_j / sum s (or scale * s_j); ids ascend.
+#pragma once
+
+#include "internal.hpp"
+
+namespace moe {
+
+constexpr int RT_MAXE = 256;  // experts supported
+constexpr int RT_EPL = RT_MAXE / WAVE;
+
+// LDS scratch of one wave's selection.  Arrays are read four entries at a
+// time (16-byte aligned, lengths padded), so loops cost one LDS round trip
+// per four values.
+struct __attribute__((aligned(16))) SelScratch {
+  float c[RT_MAXE];       // biased scores
+  float cv[RT_MAXE + 4];  // candidate biased scores, ascending expert id
+  float cs[RT_MAXE + 4];  // candidate unbiased scores s
+  int ci[RT_MAXE + 4];    // candidate expert ids
+  float g[64 + 4];        // group scores, then the kept experts' s
+};
+
+// Selection for token t from its E fp32 logits (logit[e], LDS written by this
+// wave) and the correction bias (bias[e], LDS or global).
+//
+// Top-n picks are made by rank, not by repeated arg-max: a candidate is kept
+// when fewer than n candidates beat it, where b beats a when b's key is
+// larger, or equal with a lower index.  That is a strict total order, so the
+// kept set is the one repeated arg-max with lowest-index ties would pick, and
+// every lane finds its own answer from LDS broadcast reads instead of chains
+// of cross-lane shuffles.
+__device__ inline void select_one(const RouteArgs& p, const float* logit, int64_t t,
+                                  SelScratch& z, const float* bias) {
+  const int lane = lane_id();
+  const int E = p.n_experts, G = p.n_group, Eg = E / G;
+  float s[RT_EPL], c[RT_EPL];
+  // expert e = lane + 64 * j
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int e = lane + WAVE * j;
+    if (e < E) {
+      float l = logit[e];
+      s[j] = 1.0f / (1.0f + expf(-l));
+      c[j] = s[j] + bias[e];
+      z.c[e] = c[j];
+    } else {
+      s[j] = 0.f;
+      c[j] = -INFINITY;
+    }
+  }
+  wave_lds_sync();
+
+  // group scores: lane g sums the two largest c of its group.  b1 >= b2 are
+  // the two largest values seen (a multiset: ties count twice), updated
+  // branch-free so they stay in registers.
+  float gs = -INFINITY;
+  if (lane < G) {
+    float b1 = -INFINITY, b2 = -INFINITY;
+    const int e0 = lane * Eg;
+    if ((Eg & 3) == 0) {
+      for (int i = e0; i < e0 + Eg; i += 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&z.c[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b2 = fmaxf(b2, fminf(b1, v[q]));
+          b1 = fmaxf(b1, v[q]);
+        }
+      }
+    } else {
+      for (int i = e0; i < e0 + Eg; ++i) {
+        b2 = fmaxf(b2, fminf(b1, z.c[i]));
+        b1 = fmaxf(b1, z.c[i]);
+      }
+    }
+    gs = Eg == 1 ? b1 : b1 + b2;
+  }
+  // padded to a multiple of 4 with entries that never win
+  if (lane < ((G + 3) & ~3)) z.g[lane] = lane < G ? gs : -INFINITY;
+  wave_lds_sync();
+
+  // keep the topk_group groups
+  int grank = 0;
+  if (lane < G) {
+    for (int i = 0; i < G; i += 4) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&z.g[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        grank += (v[q] > gs || (v[q] == gs && i + q < lane)) ? 1 : 0;
+    }
+  }
+  const uint64_t gmask = ballot(lane < G && grank < p.topk_group);
+
+  // the eligible experts, compacted in ascending id order
+  int n_el = 0;
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int e = lane + WAVE * j;
+    const bool elig = e < E && ((gmask >> (e / Eg)) & 1);
+    const uint64_t b = ballot(elig);
+    if (elig) {
+      const int at = n_el + __popcll(b & lanemask_lt());
+      z.cv[at] = c[j];
+      z.cs[at] = s[j];
+      z.ci[at] = e;
+    }
+    n_el += __popcll(b);
+  }
+  if (lane < ((n_el + 3) & ~3) - n_el) {
+    z.cv[n_el + lane] = -INFINITY;
+    z.ci[n_el + lane] = 0x7FFFFFFF;
+  }
+  wave_lds_sync();
+
+  // keep the top_k of them: one candidate per lane counts those that beat it;
+  // kept candidates keep their (ascending id) order
+  int kept_before = 0;
+  for (int i0 = 0; i0 < n_el; i0 += WAVE) {
+    const int i = i0 + lane;
+    const bool have = i < n_el;
+    const float my_c = have ? z.cv[i] : 0.f;
+    const int my_e = have ? z.ci[i] : 0;
+    int rank = 0;
+    for (int m = 0; m < n_el; m += 4) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&z.cv[m]);
+      const i32x4_t id = *reinterpret_cast<const i32x4_t*>(&z.ci[m]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank += (v[q] > my_c || (v[q] == my_c && id[q] < my_e)) ? 1 : 0;
+    }
+    const bool keep = have && rank < p.top_k;
+    const uint64_t b = ballot(keep);
+    if (keep) {
+      const int pos = kept_before + __popcll(b & lanemask_lt());
+      if (pos < p.top_k) {  // holds for finite scores; guards the writes otherwise
+        z.g[pos] = z.cs[i];
+        p.topk_idx[t * p.top_k + pos] = my_e;
+      }
+    }
+    kept_before += __popcll(b);
+  }
+  // zero padding up to a multiple of 4 (adding +0 after the terms changes no sum)
+  if (lane >= p.top_k && lane < ((p.top_k + 3) & ~3)) z.g[lane] = 0.0f;
+  wave_lds_sync();
+  if (lane < p.top_k) {
+    float w = z.g[lane];
+    if (p.norm_topk_prob) {
+      float denom = 0.f;  // ascending expert order
+      for (int i = 0; i < p.top_k; i += 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&z.g[i]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) denom += v[q];
+      }
+      w = p.scale * (w / denom);
+    } else {
+      w = p.scale * w;
+    }
+    p.topk_w[t * p.top_k + lane] = w;
+  }
+  wave_lds_sync();
+}
+
+}  // namespace moe
