@@ -29,7 +29,6 @@ namespace moe {
 
 namespace {
 
-constexpr int G_THREADS = 256;
 constexpr int BKB = 128;             // K bytes per stage and row
 constexpr int LDS_STRIDE = BKB + 16; // padded LDS row
 
@@ -117,10 +116,27 @@ __device__ __forceinline__ GemmProblem pick_problem(const GemmArgs& pa, bool sec
   return p;
 }
 
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8), and each XCD has its own L2.  The chip as a whole works through a
+// window of about `resident` consecutive tiles at a time (consecutive tiles
+// share A rows, and nearby M tiles of one expert share weight tiles through
+// the chip-wide cache); inside each window XCD x takes a contiguous slice, so
+// the tiles one L2 serves overlap as much as possible.
+__device__ __forceinline__ int xcd_tile_order(int b, int grid, int per_xcd) {
+  constexpr int XCDS = 8;
+  const int W = XCDS * per_xcd;
+  const int base = (b / W) * W;
+  const int n = min(W, grid - base);  // size of this window
+  const int r = b - base;
+  const int xcd = r % XCDS, local = r / XCDS;
+  const int per = n / XCDS, rem = n % XCDS;
+  return base + (xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local);
+}
+
 template <int BM, int BN>
-__device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t) {
-  const int mt = blockIdx.x / pa.n_tiles;
-  const int nt = blockIdx.x - mt * pa.n_tiles;
+__device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t, int bid) {
+  const int mt = bid / pa.n_tiles;
+  const int nt = bid - mt * pa.n_tiles;
   int gs;
   if (pa.sched) {
     if (mt >= pa.sched[0]) return false;
@@ -170,13 +186,14 @@ __device__ __forceinline__ void store_block(const Tile& t, f32x4_t acc, int64_t 
   }
 }
 
-template <int KIND, int BM, int BN, int WM, int WN, int EPI>
-__global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs pa) {
+template <int KIND, int BM, int BN, int WM, int WN, int EPI, int NTHR, int XCD_C>
+__global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs pa) {
+  constexpr int G_THREADS = NTHR;
   constexpr int ESZ = KindTraits<KIND>::ESZ;
   constexpr int STEP = KindTraits<KIND>::STEP;
   constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(WM * WN * WAVE == NTHR, "one wave per wave tile");
   static_assert(FM >= 1 && FN >= 1, "tile too small for the wave grid");
   constexpr int CPR = BKB / 16;  // 16-byte chunks per row and stage
   constexpr int A_CHUNKS = BM * CPR;
@@ -188,7 +205,8 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs pa) {
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
 
   Tile t;
-  if (!locate_tile<BM, BN>(pa, t)) return;
+  const int bid = XCD_C ? xcd_tile_order(blockIdx.x, gridDim.x, XCD_C) : int(blockIdx.x);
+  if (!locate_tile<BM, BN>(pa, t, bid)) return;
   const GemmProblem& p = t.p;
   const int tid = threadIdx.x;
   const int64_t kbytes = int64_t(p.k) * ESZ;
@@ -290,6 +308,137 @@ __global__ __launch_bounds__(G_THREADS) void gemm_kernel(GemmArgs pa) {
                              t.n0 + wn * (BN / WN) + j * 16 + lrow);
 }
 
+// ------------------------------------------------------------ ring kernel
+//
+// Large grouped GEMMs (hundreds of rows per expert and up): a 256 x 256 tile
+// per workgroup of 8 waves (2 along M x 4 along N, 128 x 64 each), K streamed
+// in 64-byte row slices through a ring of four LDS stages.  The slices are
+// fetched straight into LDS (global_load_lds_dwordx4: lane L of a wave's
+// instruction lands at byte 16 L of a 1 KB block) three stages ahead of their
+// use, so HBM and cache latency hide behind three stages of MFMA work and no
+// registers are spent on staging.  One barrier per stage.
+//
+// LDS layout of a stage: 16-row blocks of 1 KB, A blocks then B blocks; row r
+// of a block holds its four 16-byte chunks in the order c ^ ((r >> 2) & 3),
+// so the 16 rows a fragment read touches at one chunk hit 16 distinct bank
+// groups.  Each lane still receives the same K elements as in gemm_kernel,
+// so both kernels give identical results.
+constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 2, RG_WN = 4, RG_THREADS = 512;
+constexpr int RG_ROWB = 64;                        // K bytes per row and stage
+constexpr int RG_ABYTES = RG_BM * RG_ROWB;         // A part of a stage
+constexpr int RG_STAGE = (RG_BM + RG_BN) * RG_ROWB;  // 32 KB
+
+#define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediates (vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8).
+constexpr int WAIT_VM8 = 0x0F78;  // vmcnt(8)
+constexpr int WAIT_VM0 = 0x0F70;  // vmcnt(0)
+
+__device__ __forceinline__ void block_sync_lds() {
+  // Orders the DMA waits and LDS reads around the barrier for the compiler
+  // without the full fence of __syncthreads (which would wait for every
+  // stage in flight).
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int KIND, int EPI>
+__global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
+  constexpr int FM = RG_BM / RG_WM / 16;  // 8
+  constexpr int FN = RG_BN / RG_WN / 16;  // 4
+  static_assert(KIND == K_BF16, "the ring kernel takes bf16 operands");
+  __shared__ __attribute__((aligned(1024))) char ring[4 * RG_STAGE];
+
+  Tile t;
+  const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
+  if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
+  const GemmProblem& p = t.p;
+  const int tid = threadIdx.x;
+  const int wave = tid / WAVE;
+  const int lane = lane_id();
+  const int64_t kbytes = int64_t(p.k) * 2;
+  const int nk = static_cast<int>(kbytes / RG_ROWB);  // the host guarantees K bytes % 64 == 0
+
+  // DMA sources: wave w fetches 16-row blocks w and w + 8 of A and of B.  Lane
+  // L covers row L >> 2 of a block and LDS chunk slot L & 3, which holds
+  // global chunk (L & 3) ^ swizzle.  Rows past the group end (A) or past N
+  // (B) re-read the last valid row: they feed only outputs that are never
+  // stored.
+  const int r_in = lane >> 2;
+  const int chunk = (lane & 3) ^ ((r_in >> 2) & 3);
+  const char* src_a[2];
+  const char* src_b[2];
+  const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = (wave + 8 * q) * 16 + r_in;
+    const int64_t r = min<int64_t>(t.m0 + row, t.gend - 1);
+    src_a[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
+    const int n = min(t.n0 + row, p.n - 1);
+    src_b[q] = wbase + int64_t(n) * kbytes + chunk * 16;
+  }
+  auto dma = [&](int s, char* buf) {
+    const int64_t kb = int64_t(min(s, nk - 1)) * RG_ROWB;  // past the end: harmless re-read
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      __builtin_amdgcn_global_load_lds(src_a[q] + kb, MOE_LDS_PTR(buf + (wave + 8 * q) * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(src_b[q] + kb,
+                                       MOE_LDS_PTR(buf + RG_ABYTES + (wave + 8 * q) * 1024), 16,
+                                       0, 0);
+    }
+  };
+
+  const int wm = wave / RG_WN;
+  const int wn = wave % RG_WN;
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int lofs = lrow * RG_ROWB + ((lgrp ^ ((lrow >> 2) & 3)) * 16);
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const char* buf) {
+    i32x4_t af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[i] = *reinterpret_cast<const i32x4_t*>(buf + (wm * FM + i) * 1024 + lofs);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bfr[j] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn * FN + j) * 1024 + lofs);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+  };
+
+  // Stage s lives in ring slot s & 3.  Each wave has 4 DMA instructions per
+  // stage; at the wait for stage s the stages s+1 and s+2 (8 instructions)
+  // may still be in flight.
+  dma(0, ring);
+  dma(1, ring + RG_STAGE);
+  dma(2, ring + 2 * RG_STAGE);
+  for (int s = 0; s < nk; ++s) {
+    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+    block_sync_lds();  // stage s is in LDS; slot (s + 3) & 3 = (s - 1) & 3 is free
+    dma(s + 3, ring + ((s + 3) & 3) * RG_STAGE);
+    compute(ring + (s & 3) * RG_STAGE);
+  }
+  // no LDS write may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      store_block<KIND, EPI>(t, acc[i][j], t.m0 + wm * (RG_BM / RG_WM) + i * 16 + lgrp * 4,
+                             t.n0 + wn * (RG_BN / RG_WN) + j * 16 + lrow);
+}
+
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
   const int64_t row = int64_t(blockIdx.x) * 4 + threadIdx.x / WAVE;
@@ -338,14 +487,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
 template <int KIND, int EPI>
 hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
                            Timing t) {
+  const dim3 g(grid);
   if (shape.bm == 16)
-    return launch_k(gemm_kernel<KIND, 16, 128, 1, 4, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
-                    p);
+    return launch_k(gemm_kernel<KIND, 16, 128, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if (shape.bm == 64)
-    return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
-                    p);
-  return launch_k(gemm_kernel<KIND, 128, 128, 2, 2, EPI>, dim3(grid), dim3(G_THREADS), stream, t,
-                  p);
+    return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI, 256, 0>, g, dim3(256), stream, t, p);
+  if constexpr (KIND == K_BF16) {
+    if (shape.bm == RG_BM)
+      return launch_k(gemm_ring_kernel<KIND, EPI>, g, dim3(RG_THREADS), stream, t, p);
+  }
+  if constexpr (KIND == K_FP8) {
+    if (shape.bm == 256)
+      return launch_k(gemm_kernel<KIND, 256, 256, 2, 4, EPI, 512, 32>, g, dim3(512), stream, t,
+                      p);
+  }
+  // two workgroups per CU: 64 tiles per XCD in flight
+  return launch_k(gemm_kernel<KIND, 128, 128, 2, 2, EPI, 256, 64>, g, dim3(256), stream, t, p);
 }
 
 template <int KIND>
@@ -358,11 +515,11 @@ hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned gri
 }  // namespace
 
 GemmShape pick_gemm_shape(int kind, int64_t rows, int groups) {
-  (void)kind;
   const int64_t avg = groups > 0 ? rows / groups : rows;
   if (avg <= 24) return GemmShape{16, 128};
   if (avg <= 80) return GemmShape{64, 128};
-  return GemmShape{128, 128};
+  if (avg < 128 || kind == K_F32) return GemmShape{128, 128};
+  return GemmShape{256, 256};
 }
 
 int64_t max_mtiles(int64_t rows, int groups, int bm) {

@@ -29,15 +29,31 @@ def rms(a) -> float:
     return float(np.sqrt(np.mean(np.square(np.asarray(a, np.float64)))))
 
 
-def assert_close_rms(got, ref, what: str, max_tol=MAX_TOL, mean_tol=MEAN_TOL, R=None):
+def assert_close_rms(got, ref, what: str, max_tol=MAX_TOL, mean_tol=MEAN_TOL, R=None,
+                     row_allow=None):
+    """max-abs <= max_tol R and mean-abs <= mean_tol R, R = RMS of ref.
+
+    row_allow: optional per-row extra absolute allowance of the max-abs gate
+    (fp8 rounding flips, see fp8_flips); the mean gate is unchanged."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     R = rms(ref) if R is None else R
     err = np.abs(got - ref)
     mx, mn = err.max() / R, err.mean() / R
     print(f"{what}: max/R={mx:.3e} mean/R={mn:.3e} R={R:.4g}", flush=True)
-    assert mx <= max_tol, f"{what}: max-abs error {mx:.3e} of RMS exceeds {max_tol}"
     assert mn <= mean_tol, f"{what}: mean-abs error {mn:.3e} of RMS exceeds {mean_tol}"
+    if row_allow is None:
+        assert mx <= max_tol, f"{what}: max-abs error {mx:.3e} of RMS exceeds {max_tol}"
+        return
+    row_err = err.reshape(err.shape[0], -1).max(axis=1)
+    allow = np.asarray(row_allow, np.float64)
+    over = row_err > max_tol * R
+    print(f"{what}: {int((allow > 0).sum())} of {allow.size} rows have e4m3 values near a "
+          f"rounding midpoint, {int(over.sum())} of them beyond the plain gate", flush=True)
+    bad = np.flatnonzero(row_err > max_tol * R + allow)
+    assert bad.size == 0, (f"{what}: rows {bad[:8].tolist()} exceed max_tol R + allowance "
+                           f"(err/R {(row_err[bad[:8]] / R).round(4).tolist()}, "
+                           f"allowance/R {(allow[bad[:8]] / R).round(4).tolist()})")
 
 
 def assert_routing_equal(gpu_idx, gpu_w, ref_idx, ref_w, margin, what: str):

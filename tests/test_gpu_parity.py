@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import fp8_flips
 from gpu_util import (assert_close_rms, assert_routing_equal, rms, to_f64, upload)
 from non_gated_relu_amd import binding
 from non_gated_relu_amd.synthetic import WORKLOADS, Workload, make_inputs
@@ -22,9 +23,16 @@ ALL_GROUPS = Workload("all-groups-T33", 33, 128, 64, 8, 8, 8, 128, 64, "bf16", "
 WHOLE_GROUP = Workload("k-fills-group-T50", 50, 128, 32, 4, 1, 8, 64, 0, "bf16", "bf16", seed=25)
 BIG_ROWS = Workload("many-rows-T600", 600, 128, 16, 2, 1, 2, 128, 128, "bf16", "bf16", seed=26)
 SINGLE = dataclasses.replace(WORKLOADS["decode-bf16-T32"], name="decode-bf16-T1", tokens=1)
+# Hundreds of rows per expert: the 256 x 256 tile kernels (I = 320 leaves a
+# partial N tile; d = 64 gives a K loop shorter than the DMA ring).
+BIG_GROUPS_BF16 = Workload("big-groups-bf16-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16",
+                           "bf16", seed=27)
+BIG_GROUPS_FP8 = Workload("big-groups-fp8-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp8",
+                          seed=28)
+SHORT_K = Workload("big-groups-bf16-d64", 1024, 64, 16, 4, 1, 2, 128, 64, "bf16", "bf16", seed=29)
 
 SMALL = [WORKLOADS["tiny-f32-T64"], RAGGED_BF16, RAGGED_FP8, PLAIN_TOPK, ALL_GROUPS, WHOLE_GROUP,
-         BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE]
+         BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE, BIG_GROUPS_BF16, BIG_GROUPS_FP8, SHORT_K]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -87,7 +95,14 @@ def test_small_layer_every_entry_point(wl):
     ffn_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, rows, mats, inp["w_up"], inp["w_down"],
                               wl.expert_dtype, inp["w_up_scale"], inp["w_down_scale"],
                               quant_a=wl.expert_dtype == "fp8")
-    assert_close_rms(to_f64(parts["y_perm"]), ffn_ref, f"{wl.name} expert_ffn", **_tol(wl))
+    allow_rows = allow_tok = None
+    if wl.expert_dtype == "fp8":
+        allow_rows = fp8_flips.row_allowance(inp["x"], rows, mats, inp["w_up"], inp["w_up_scale"],
+                                             inp["w_down"], inp["w_down_scale"])
+        allow_tok = fp8_flips.token_allowance(allow_rows, parts["w"].cpu().numpy(),
+                                              slot_pos.reshape(T, k))
+    assert_close_rms(to_f64(parts["y_perm"]), ffn_ref, f"{wl.name} expert_ffn", **_tol(wl),
+                     row_allow=allow_rows)
     if wl.shared_inter:
         sh_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, np.arange(T), np.zeros(T),
                                  inp["ws_up"][None], inp["ws_down"][None], wl.act_dtype)
@@ -99,7 +114,7 @@ def test_small_layer_every_entry_point(wl):
     ulp = 2.0 ** -8 if wl.act_dtype == "bf16" else 2.0 ** -22
     assert (np.abs(got - comb_ref) <= ulp * np.abs(comb_ref) + 1e-6 * rms(comb_ref)).all()
     # the layer against the oracle
-    assert_close_rms(got, ref["y"], f"{wl.name} layer", **_tol(wl))
+    assert_close_rms(got, ref["y"], f"{wl.name} layer", **_tol(wl), row_allow=allow_tok)
 
     # the fused entry point equals the composition bit for bit
     y = binding.forward(cfg, t["x"], t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
@@ -229,3 +244,39 @@ def test_graph_replays_match_eager(wl):
     torch.cuda.synchronize()
     assert torch.equal(_bits(y), _bits(ref))
     del other
+
+
+@pytest.mark.parametrize("wl", [BIG_GROUPS_BF16, BIG_GROUPS_FP8], ids=lambda w: w.name)
+def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
+    """A row's result is the same whichever tile shape computes it: a call
+    with hundreds of rows per expert (256-row tiles) and a call with a few
+    rows (16-row tiles) give identical bits for the rows they share."""
+    print(f"case {wl.name}", flush=True)
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    cfg = binding.config_from(wl)
+    T = wl.tokens
+    rng = np.random.default_rng(7)
+    src = torch.from_numpy(rng.integers(0, T, size=1200).astype(np.int32)).cuda()
+    sc = dict(w_dtype=wl.expert_dtype, w_up_scale=t.get("w_up_scale"),
+              w_down_scale=t.get("w_down_scale"))
+    big_off = torch.tensor([0, 700, 1200], dtype=torch.int32, device="cuda")
+    big = binding.expert_ffn(cfg, t["w_up"][:2], t["w_down"][:2], t["x"], big_off, 1200,
+                             row_index=src, **sc)
+    pick = torch.tensor([0, 5, 699, 700, 1199], device="cuda").long()
+    small_off = torch.tensor([0, 3, 5], dtype=torch.int32, device="cuda")
+    small = binding.expert_ffn(cfg, t["w_up"][:2], t["w_down"][:2], t["x"], small_off, 5,
+                               row_index=src[pick].contiguous(), **sc)
+    torch.cuda.synchronize()
+    assert torch.equal(big[pick], small)
+    mats = np.repeat([0, 1], [700, 500])
+    ref = oracle.ffn_rows(inp["x"], wl.act_dtype, src.cpu().numpy(), mats, inp["w_up"][:2],
+                          inp["w_down"][:2], wl.expert_dtype,
+                          None if inp["w_up_scale"] is None else inp["w_up_scale"][:2],
+                          None if inp["w_down_scale"] is None else inp["w_down_scale"][:2],
+                          quant_a=wl.expert_dtype == "fp8")
+    allow = None
+    if wl.expert_dtype == "fp8":
+        allow = fp8_flips.row_allowance(inp["x"], src.cpu().numpy(), mats, inp["w_up"],
+                                        inp["w_up_scale"], inp["w_down"], inp["w_down_scale"])
+    assert_close_rms(to_f64(big), ref, f"{wl.name} expert_ffn 256-row tiles", row_allow=allow)
