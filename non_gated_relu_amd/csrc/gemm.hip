@@ -23,6 +23,8 @@
 // Every output element accumulates its K steps in ascending order with the
 // same MFMA, whichever tile shape computes it, so results do not depend on
 // the launch configuration.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace moe {
@@ -319,19 +321,25 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs pa) {
 // registers are spent on staging.  One barrier per stage.
 //
 // LDS layout of a stage: 16-row blocks of 1 KB, A blocks then B blocks; row r
-// of a block holds its four 16-byte chunks in the order c ^ ((r >> 2) & 3),
-// so the 16 rows a fragment read touches at one chunk hit 16 distinct bank
-// groups.  Each lane still receives the same K elements as in gemm_kernel,
-// so both kernels give identical results.
+// of a block holds its 16-byte chunk c in slot c ^ swz(r), swz(r) =
+// ((r >> 1) ^ (r >> 3)) & 3.  A fragment read has the 16 lanes of a chunk on
+// rows 0..15; with this swizzle every 8 consecutive lanes cover the 32 banks
+// once and every 16 cover 64 banks once, so the read is conflict-free whether
+// the LDS serves 8 or 16 lanes of a 16-byte read per clock.  Each lane still
+// receives the same K elements as in gemm_kernel, so both kernels give
+// identical results.
 constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 2, RG_WN = 4, RG_THREADS = 512;
 constexpr int RG_ROWB = 64;                        // K bytes per row and stage
 constexpr int RG_ABYTES = RG_BM * RG_ROWB;         // A part of a stage
 constexpr int RG_STAGE = (RG_BM + RG_BN) * RG_ROWB;  // 32 KB
 
+__device__ __forceinline__ int rg_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt immediates (vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8).
 constexpr int WAIT_VM8 = 0x0F78;  // vmcnt(8)
+constexpr int WAIT_VM4_LGKM0 = 0x0074;  // vmcnt(4) lgkmcnt(0)
 constexpr int WAIT_VM0 = 0x0F70;  // vmcnt(0)
 
 __device__ __forceinline__ void block_sync_lds() {
@@ -366,7 +374,7 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
   // (B) re-read the last valid row: they feed only outputs that are never
   // stored.
   const int r_in = lane >> 2;
-  const int chunk = (lane & 3) ^ ((r_in >> 2) & 3);
+  const int chunk = (lane & 3) ^ rg_swizzle(r_in);
   const char* src_a[2];
   const char* src_b[2];
   const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
@@ -378,23 +386,38 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
     const int n = min(t.n0 + row, p.n - 1);
     src_b[q] = wbase + int64_t(n) * kbytes + chunk * 16;
   }
-  auto dma = [&](int s, char* buf) {
+  // DMA instruction q (0..3) of stage s into ring slot buf: the A blocks
+  // wave and wave + 8, then the B blocks.
+  auto dma_one = [&](int q, int s, char* buf) {
     const int64_t kb = int64_t(min(s, nk - 1)) * RG_ROWB;  // past the end: harmless re-read
+    const int blk = wave + 8 * (q & 1);
+    if (q < 2)
+      __builtin_amdgcn_global_load_lds(src_a[q & 1] + kb, MOE_LDS_PTR(buf + blk * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(src_b[q & 1] + kb,
+                                       MOE_LDS_PTR(buf + RG_ABYTES + blk * 1024), 16, 0, 0);
+  };
+  auto dma = [&](int s, char* buf) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds(src_a[q] + kb, MOE_LDS_PTR(buf + (wave + 8 * q) * 1024), 16,
-                                       0, 0);
-      __builtin_amdgcn_global_load_lds(src_b[q] + kb,
-                                       MOE_LDS_PTR(buf + RG_ABYTES + (wave + 8 * q) * 1024), 16,
-                                       0, 0);
-    }
+    for (int q = 0; q < 4; ++q) dma_one(q, s, buf);
   };
 
   const int wm = wave / RG_WN;
   const int wn = wave % RG_WN;
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  const int lofs = lrow * RG_ROWB + ((lgrp ^ ((lrow >> 2) & 3)) * 16);
+  const int lofs = lrow * RG_ROWB + ((lgrp ^ rg_swizzle(lrow)) * 16);
+
+  // Work skipped in partial tiles.  Wave (wm, wn) owns rows wm*128 + [0, 128)
+  // and the 16-column blocks wn + 4 j.  Rows: a wave drops its fragments past
+  // the tile's last row; each SIMD runs one wave of each half, so its MFMA
+  // time follows the valid rows.  Columns: in the last N tile the valid blocks
+  // are dealt round-robin, so every SIMD keeps about the same share.
+  const int rows_valid = static_cast<int>(min<int64_t>(t.gend - t.m0, RG_BM));
+  const int fm_valid = min(max((rows_valid - wm * (RG_BM / RG_WM) + 15) / 16, 0), FM);
+  const int nblk = (min(p.n - t.n0, RG_BN) + 15) / 16;
+  const int fn_valid = min(max((nblk - wn + RG_WN - 1) / RG_WN, 0), FN);
+  const bool full_n = nblk * 16 >= RG_BN;
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -402,41 +425,98 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const char* buf) {
-    i32x4_t af[FM], bfr[FN];
+  // Fragment reads and MFMAs of one stage, in four quarters: quarter q reads
+  // B fragment q and A fragments 2q, 2q + 1, and does the MFMAs of A rows
+  // 2q, 2q + 1 (FMV row fragments in all; all columns when FULL_N, else the
+  // first fn_valid column fragments).
+  auto load_quarter = [&](int q, const char* buf, i32x4_t (&af)[FM], i32x4_t (&bf)[FN],
+                          auto fmv_c, auto full_c) {
+    constexpr int FMV = decltype(fmv_c)::value;
+    constexpr bool FULL_N = decltype(full_c)::value;
+    if (FULL_N || q < fn_valid)
+      bf[q] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn + RG_WN * q) * 1024 + lofs);
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      af[i] = *reinterpret_cast<const i32x4_t*>(buf + (wm * FM + i) * 1024 + lofs);
+    for (int i = 2 * q; i < 2 * q + 2; ++i)
+      if (i < FMV) af[i] = *reinterpret_cast<const i32x4_t*>(buf + (wm * FM + i) * 1024 + lofs);
+  };
+  auto mma_quarter = [&](int q, const i32x4_t (&af)[FM], const i32x4_t (&bf)[FN], auto fmv_c,
+                         auto full_c) {
+    constexpr int FMV = decltype(fmv_c)::value;
+    constexpr bool FULL_N = decltype(full_c)::value;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      bfr[j] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn * FN + j) * 1024 + lofs);
+    for (int i = 2 * q; i < 2 * q + 2; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j)
+        if (i < FMV && (FULL_N || j < fn_valid)) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
   };
 
-  // Stage s lives in ring slot s & 3.  Each wave has 4 DMA instructions per
-  // stage; at the wait for stage s the stages s+1 and s+2 (8 instructions)
-  // may still be in flight.
-  dma(0, ring);
-  dma(1, ring + RG_STAGE);
-  dma(2, ring + 2 * RG_STAGE);
-  for (int s = 0; s < nk; ++s) {
+  // Stage s lives in ring slot s & 3 and is fetched three stages ahead.  Its
+  // fragments are read from LDS one stage ahead, during the MFMAs of stage
+  // s - 1, so LDS latency hides behind MFMA work.  At the top of step s the
+  // wave waits for its DMA of stage s+1 (stage s+2, 4 instructions, may still
+  // fly) and for its fragment reads of stage s, issued a whole step earlier
+  // (so that nothing waits on the reads it issues next); the barrier then
+  // makes stage s+1 visible to all waves and ensures slot (s + 3) & 3, read
+  // for stage s-1 during step s-2, is free.  The step's DMA and LDS reads are
+  // spread between its MFMAs (one DMA, three reads, a quarter of the MFMAs at
+  // a time) so that no burst of memory instructions holds up MFMA issue.
+  auto step = [&](int s, const i32x4_t (&ca)[FM], const i32x4_t (&cb)[FN], i32x4_t (&na)[FM],
+                  i32x4_t (&nb)[FN], auto fmv_c, auto full_c) {
+    __builtin_amdgcn_s_waitcnt(WAIT_VM4_LGKM0);
+    block_sync_lds();
+    char* dbuf = ring + ((s + 3) & 3) * RG_STAGE;
+    const char* nbuf = ring + ((s + 1) & 3) * RG_STAGE;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma_one(q, s + 3, dbuf);
+      load_quarter(q, nbuf, na, nb, fmv_c, full_c);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+      mma_quarter(q, ca, cb, fmv_c, full_c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto k_loop = [&](auto fmv_c, auto full_c) {
+    i32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+    dma(0, ring);
+    dma(1, ring + RG_STAGE);
+    dma(2, ring + 2 * RG_STAGE);
     __builtin_amdgcn_s_waitcnt(WAIT_VM8);
-    block_sync_lds();  // stage s is in LDS; slot (s + 3) & 3 = (s - 1) & 3 is free
-    dma(s + 3, ring + ((s + 3) & 3) * RG_STAGE);
-    compute(ring + (s & 3) * RG_STAGE);
-  }
-  // no LDS write may still be in flight when the workgroup ends
-  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+    block_sync_lds();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_quarter(q, ring, a0, b0, fmv_c, full_c);
+    for (int s = 0; s < nk; s += 2) {
+      step(s, a0, b0, a1, b1, fmv_c, full_c);
+      if (s + 1 >= nk) break;
+      step(s + 1, a1, b1, a0, b0, fmv_c, full_c);
+    }
+    // no LDS write may still be in flight when the workgroup ends
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  };
+  auto with_rows = [&](auto full_c) {
+    using I = int;
+    switch (fm_valid) {
+      case 8: k_loop(std::integral_constant<I, 8>{}, full_c); break;
+      case 7: k_loop(std::integral_constant<I, 7>{}, full_c); break;
+      case 6: k_loop(std::integral_constant<I, 6>{}, full_c); break;
+      case 5: k_loop(std::integral_constant<I, 5>{}, full_c); break;
+      case 4: k_loop(std::integral_constant<I, 4>{}, full_c); break;
+      case 3: k_loop(std::integral_constant<I, 3>{}, full_c); break;
+      case 2: k_loop(std::integral_constant<I, 2>{}, full_c); break;
+      case 1: k_loop(std::integral_constant<I, 1>{}, full_c); break;
+      default: k_loop(std::integral_constant<I, 0>{}, full_c); break;
+    }
+  };
+  if (full_n)
+    with_rows(std::true_type{});
+  else
+    with_rows(std::false_type{});
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       store_block<KIND, EPI>(t, acc[i][j], t.m0 + wm * (RG_BM / RG_WM) + i * 16 + lgrp * 4,
-                             t.n0 + wn * (RG_BN / RG_WN) + j * 16 + lrow);
+                             t.n0 + (wn + RG_WN * j) * 16 + lrow);
 }
 
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
