@@ -27,6 +27,9 @@
 
 #include "internal.hpp"
 
+#ifndef MOE_RING_WAVES
+#define MOE_RING_WAVES 8
+#endif
 namespace moe {
 
 namespace {
@@ -328,19 +331,21 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs pa) {
 // the LDS serves 8 or 16 lanes of a 16-byte read per clock.  Each lane still
 // receives the same K elements as in gemm_kernel, so both kernels give
 // identical results.
-constexpr int RG_BM = 256, RG_BN = 256, RG_WM = 2, RG_WN = 4, RG_THREADS = 512;
-constexpr int RG_ROWB = 64;                        // K bytes per row and stage
-constexpr int RG_ABYTES = RG_BM * RG_ROWB;         // A part of a stage
+constexpr int RG_BM = 256, RG_BN = 256;
+constexpr int RG_ROWB = 64;                          // K bytes per row and stage
+constexpr int RG_ABYTES = RG_BM * RG_ROWB;           // A part of a stage
 constexpr int RG_STAGE = (RG_BM + RG_BN) * RG_ROWB;  // 32 KB
+constexpr int RG_BLOCKS = (RG_BM + RG_BN) / 16;      // 1 KB blocks per stage
 
 __device__ __forceinline__ int rg_swizzle(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt immediates (vmcnt in bits 3:0, expcnt 6:4, lgkmcnt 11:8).
-constexpr int WAIT_VM8 = 0x0F78;  // vmcnt(8)
-constexpr int WAIT_VM4_LGKM0 = 0x0074;  // vmcnt(4) lgkmcnt(0)
-constexpr int WAIT_VM0 = 0x0F70;  // vmcnt(0)
+// s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+constexpr int WAIT_VM0 = waitcnt_imm(0, 15);
 
 __device__ __forceinline__ void block_sync_lds() {
   // Orders the DMA waits and LDS reads around the barrier for the compiler
@@ -351,72 +356,75 @@ __device__ __forceinline__ void block_sync_lds() {
   __asm__ volatile("" ::: "memory");
 }
 
-template <int KIND, int EPI>
-__global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
-  constexpr int FM = RG_BM / RG_WM / 16;  // 8
-  constexpr int FN = RG_BN / RG_WN / 16;  // 4
+// NW waves in a 2 x (NW / 2) grid; wave (wm, wn) owns the 16-row blocks
+// wm + 2 i and the 16-column blocks wn + (NW / 2) j of the tile, dealt
+// round-robin so that partial tiles leave every SIMD about the same work.
+template <int KIND, int EPI, int NW>
+__global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
+  constexpr int WM = 2, WN = NW / 2;
+  constexpr int FM = RG_BM / WM / 16;  // 8
+  constexpr int FN = RG_BN / WN / 16;  // 4 (8 waves) or 8 (4 waves)
+  constexpr int DMA_PER_WAVE = RG_BLOCKS / NW;  // per stage
+  constexpr int QUARTERS = 4;
   static_assert(KIND == K_BF16, "the ring kernel takes bf16 operands");
+  static_assert(DMA_PER_WAVE % QUARTERS == 0 && FN % QUARTERS == 0, "quarter split");
   __shared__ __attribute__((aligned(1024))) char ring[4 * RG_STAGE];
 
   Tile t;
   const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
   if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
   const GemmProblem& p = t.p;
-  const int tid = threadIdx.x;
-  const int wave = tid / WAVE;
+  const int wave = threadIdx.x / WAVE;
   const int lane = lane_id();
   const int64_t kbytes = int64_t(p.k) * 2;
   const int nk = static_cast<int>(kbytes / RG_ROWB);  // the host guarantees K bytes % 64 == 0
 
-  // DMA sources: wave w fetches 16-row blocks w and w + 8 of A and of B.  Lane
-  // L covers row L >> 2 of a block and LDS chunk slot L & 3, which holds
-  // global chunk (L & 3) ^ swizzle.  Rows past the group end (A) or past N
-  // (B) re-read the last valid row: they feed only outputs that are never
-  // stored.
+  // DMA sources: wave w fetches the 16-row blocks w + NW q of the stage
+  // (blocks 0..15 are A rows, 16..31 B rows).  Lane L covers row L >> 2 of a
+  // block and LDS chunk slot L & 3, which holds global chunk (L & 3) ^
+  // swizzle.  Rows past the group end (A) or past N (B) re-read the last
+  // valid row: they feed only outputs that are never stored.
   const int r_in = lane >> 2;
   const int chunk = (lane & 3) ^ rg_swizzle(r_in);
-  const char* src_a[2];
-  const char* src_b[2];
   const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
+  const char* src[DMA_PER_WAVE];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = (wave + 8 * q) * 16 + r_in;
-    const int64_t r = min<int64_t>(t.m0 + row, t.gend - 1);
-    src_a[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
-    const int n = min(t.n0 + row, p.n - 1);
-    src_b[q] = wbase + int64_t(n) * kbytes + chunk * 16;
+  for (int q = 0; q < DMA_PER_WAVE; ++q) {
+    const int blk = wave + NW * q;
+    const int row = (blk % 16) * 16 + r_in;
+    if (blk < 16) {
+      const int64_t r = min<int64_t>(t.m0 + row, t.gend - 1);
+      src[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
+    } else {
+      const int n = min(t.n0 + row, p.n - 1);
+      src[q] = wbase + int64_t(n) * kbytes + chunk * 16;
+    }
   }
-  // DMA instruction q (0..3) of stage s into ring slot buf: the A blocks
-  // wave and wave + 8, then the B blocks.
   auto dma_one = [&](int q, int s, char* buf) {
     const int64_t kb = int64_t(min(s, nk - 1)) * RG_ROWB;  // past the end: harmless re-read
-    const int blk = wave + 8 * (q & 1);
-    if (q < 2)
-      __builtin_amdgcn_global_load_lds(src_a[q & 1] + kb, MOE_LDS_PTR(buf + blk * 1024), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(src_b[q & 1] + kb,
-                                       MOE_LDS_PTR(buf + RG_ABYTES + blk * 1024), 16, 0, 0);
+    // (through a plain pointer: clang drops the host launch stub of this
+    // template when an element of the dependently sized array is passed to
+    // the builtin directly)
+    const void* from = src[q] + kb;
+    __builtin_amdgcn_global_load_lds(from, MOE_LDS_PTR(buf + (wave + NW * q) * 1024), 16, 0, 0);
   };
   auto dma = [&](int s, char* buf) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dma_one(q, s, buf);
+    for (int q = 0; q < DMA_PER_WAVE; ++q) dma_one(q, s, buf);
   };
 
-  const int wm = wave / RG_WN;
-  const int wn = wave % RG_WN;
+  const int wm = wave % WM;
+  const int wn = wave / WM;
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
   const int lofs = lrow * RG_ROWB + ((lgrp ^ rg_swizzle(lrow)) * 16);
 
-  // Work skipped in partial tiles.  Wave (wm, wn) owns rows wm*128 + [0, 128)
-  // and the 16-column blocks wn + 4 j.  Rows: a wave drops its fragments past
-  // the tile's last row; each SIMD runs one wave of each half, so its MFMA
-  // time follows the valid rows.  Columns: in the last N tile the valid blocks
-  // are dealt round-robin, so every SIMD keeps about the same share.
-  const int rows_valid = static_cast<int>(min<int64_t>(t.gend - t.m0, RG_BM));
-  const int fm_valid = min(max((rows_valid - wm * (RG_BM / RG_WM) + 15) / 16, 0), FM);
+  // Work skipped in partial tiles: fragments whose 16 rows all lie past the
+  // group end, or whose 16 columns all lie past N.
+  const int mblk = static_cast<int>((min<int64_t>(t.gend - t.m0, RG_BM) + 15) / 16);
+  const int fm_valid = min(max((mblk - wm + WM - 1) / WM, 0), FM);
   const int nblk = (min(p.n - t.n0, RG_BN) + 15) / 16;
-  const int fn_valid = min(max((nblk - wn + RG_WN - 1) / RG_WN, 0), FN);
+  const int fn_valid = min(max((nblk - wn + WN - 1) / WN, 0), FN);
   const bool full_n = nblk * 16 >= RG_BN;
 
   f32x4_t acc[FM][FN];
@@ -426,18 +434,20 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Fragment reads and MFMAs of one stage, in four quarters: quarter q reads
-  // B fragment q and A fragments 2q, 2q + 1, and does the MFMAs of A rows
-  // 2q, 2q + 1 (FMV row fragments in all; all columns when FULL_N, else the
-  // first fn_valid column fragments).
+  // B fragments [q FN/4, (q+1) FN/4) and A fragments 2q, 2q + 1, and does the
+  // MFMAs of A rows 2q, 2q + 1 (FMV row fragments in all; all columns when
+  // FULL_N, else the first fn_valid column fragments).
   auto load_quarter = [&](int q, const char* buf, i32x4_t (&af)[FM], i32x4_t (&bf)[FN],
                           auto fmv_c, auto full_c) {
     constexpr int FMV = decltype(fmv_c)::value;
     constexpr bool FULL_N = decltype(full_c)::value;
-    if (FULL_N || q < fn_valid)
-      bf[q] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn + RG_WN * q) * 1024 + lofs);
+#pragma unroll
+    for (int j = q * (FN / QUARTERS); j < (q + 1) * (FN / QUARTERS); ++j)
+      if (FULL_N || j < fn_valid)
+        bf[j] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn + WN * j) * 1024 + lofs);
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i)
-      if (i < FMV) af[i] = *reinterpret_cast<const i32x4_t*>(buf + (wm * FM + i) * 1024 + lofs);
+      if (i < FMV) af[i] = *reinterpret_cast<const i32x4_t*>(buf + (wm + WM * i) * 1024 + lofs);
   };
   auto mma_quarter = [&](int q, const i32x4_t (&af)[FM], const i32x4_t (&bf)[FN], auto fmv_c,
                          auto full_c) {
@@ -453,22 +463,26 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
   // Stage s lives in ring slot s & 3 and is fetched three stages ahead.  Its
   // fragments are read from LDS one stage ahead, during the MFMAs of stage
   // s - 1, so LDS latency hides behind MFMA work.  At the top of step s the
-  // wave waits for its DMA of stage s+1 (stage s+2, 4 instructions, may still
-  // fly) and for its fragment reads of stage s, issued a whole step earlier
-  // (so that nothing waits on the reads it issues next); the barrier then
-  // makes stage s+1 visible to all waves and ensures slot (s + 3) & 3, read
-  // for stage s-1 during step s-2, is free.  The step's DMA and LDS reads are
-  // spread between its MFMAs (one DMA, three reads, a quarter of the MFMAs at
-  // a time) so that no burst of memory instructions holds up MFMA issue.
+  // wave waits for its DMA of stage s+1 (stage s+2 may still fly) and for its
+  // fragment reads of stage s, issued a whole step earlier (so that nothing
+  // waits on the reads it issues next); the barrier then makes stage s+1
+  // visible to all waves and ensures slot (s + 3) & 3, read for stage s-1
+  // during step s-2, is free.  The step's DMA and LDS reads are spread
+  // between its MFMAs, a quarter at a time, so that no burst of memory
+  // instructions holds up MFMA issue.
+  constexpr int WAIT_NEXT = waitcnt_imm(DMA_PER_WAVE, 0);
+  constexpr int WAIT_FIRST = waitcnt_imm(2 * DMA_PER_WAVE, 15);
   auto step = [&](int s, const i32x4_t (&ca)[FM], const i32x4_t (&cb)[FN], i32x4_t (&na)[FM],
                   i32x4_t (&nb)[FN], auto fmv_c, auto full_c) {
-    __builtin_amdgcn_s_waitcnt(WAIT_VM4_LGKM0);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
     block_sync_lds();
     char* dbuf = ring + ((s + 3) & 3) * RG_STAGE;
     const char* nbuf = ring + ((s + 1) & 3) * RG_STAGE;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      dma_one(q, s + 3, dbuf);
+    for (int q = 0; q < QUARTERS; ++q) {
+#pragma unroll
+      for (int d = q * (DMA_PER_WAVE / QUARTERS); d < (q + 1) * (DMA_PER_WAVE / QUARTERS); ++d)
+        dma_one(d, s + 3, dbuf);
       load_quarter(q, nbuf, na, nb, fmv_c, full_c);
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
       mma_quarter(q, ca, cb, fmv_c, full_c);
@@ -480,10 +494,10 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
     dma(0, ring);
     dma(1, ring + RG_STAGE);
     dma(2, ring + 2 * RG_STAGE);
-    __builtin_amdgcn_s_waitcnt(WAIT_VM8);
+    __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
     block_sync_lds();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) load_quarter(q, ring, a0, b0, fmv_c, full_c);
+    for (int q = 0; q < QUARTERS; ++q) load_quarter(q, ring, a0, b0, fmv_c, full_c);
     for (int s = 0; s < nk; s += 2) {
       step(s, a0, b0, a1, b1, fmv_c, full_c);
       if (s + 1 >= nk) break;
@@ -515,8 +529,8 @@ __global__ __launch_bounds__(RG_THREADS) void gemm_ring_kernel(GemmArgs pa) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      store_block<KIND, EPI>(t, acc[i][j], t.m0 + wm * (RG_BM / RG_WM) + i * 16 + lgrp * 4,
-                             t.n0 + (wn + RG_WN * j) * 16 + lrow);
+      store_block<KIND, EPI>(t, acc[i][j], t.m0 + (wm + WM * i) * 16 + lgrp * 4,
+                             t.n0 + (wn + WN * j) * 16 + lrow);
 }
 
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
@@ -574,7 +588,8 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
     return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if constexpr (KIND == K_BF16) {
     if (shape.bm == RG_BM)
-      return launch_k(gemm_ring_kernel<KIND, EPI>, g, dim3(RG_THREADS), stream, t, p);
+      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES>, g, dim3(MOE_RING_WAVES * WAVE),
+                      stream, t, p);
   }
   if constexpr (KIND == K_FP8) {
     if (shape.bm == 256)

@@ -145,7 +145,12 @@ hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stre
     q.index_div = 1;
     g.sched = nullptr;
     g.n_groups = 1;
-    const GemmShape shape{128, 128};
+    // The gate matrix is small (E x d) and every M tile streams all of it from
+    // L2, so tiles are as tall as keeps some 256+ workgroups in flight: short
+    // tiles at a few thousand tokens, taller ones beyond.  Every shape gives
+    // the same logits (one MFMA chain per element, K ascending).
+    const int bm = p.tokens <= 4096 ? 16 : (p.tokens <= 16384 ? 64 : 128);
+    const GemmShape shape{bm, 128};
     g.n_tiles = (p.n_experts + shape.bn - 1) / shape.bn;
     const int64_t mtiles = (p.tokens + shape.bm - 1) / shape.bm;
     e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, stream, first);
