@@ -27,6 +27,9 @@
 
 #include "internal.hpp"
 
+#ifndef MOE_FP8_RING
+#define MOE_FP8_RING 1
+#endif
 #ifndef MOE_RING_WAVES
 #define MOE_RING_WAVES 8
 #endif
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   constexpr int FN = RG_BN / WN / 16;  // 4 (8 waves) or 8 (4 waves)
   constexpr int DMA_PER_WAVE = RG_BLOCKS / NW;  // per stage
   constexpr int QUARTERS = 4;
-  static_assert(KIND == K_BF16, "the ring kernel takes bf16 operands");
+  static_assert(KIND == K_BF16 || KIND == K_FP8, "the ring kernel takes bf16 or fp8 operands");
   static_assert(DMA_PER_WAVE % QUARTERS == 0 && FN % QUARTERS == 0, "quarter split");
   __shared__ __attribute__((aligned(1024))) char ring[4 * RG_STAGE];
 
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   const GemmProblem& p = t.p;
   const int wave = threadIdx.x / WAVE;
   const int lane = lane_id();
-  const int64_t kbytes = int64_t(p.k) * 2;
+  const int64_t kbytes = int64_t(p.k) * KindTraits<KIND>::ESZ;
   const int nk = static_cast<int>(kbytes / RG_ROWB);  // the host guarantees K bytes % 64 == 0
 
   // DMA sources: wave w fetches the 16-row blocks w + NW q of the stage
@@ -412,6 +415,22 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) dma_one(q, s, buf);
   };
+
+  // fp8: the tile's row scales (activation rows) and column scales (weight
+  // rows), staged once in LDS for the epilogue; the K loop's first barrier
+  // makes them visible.
+  __shared__ float sc_row[KIND == K_FP8 ? RG_BM : 1];
+  __shared__ float sc_col[KIND == K_FP8 ? RG_BN : 1];
+  if constexpr (KIND == K_FP8) {
+    const int i = threadIdx.x;
+    if (i < RG_BM) {
+      const int64_t r = t.m0 + i;
+      sc_row[i] = r < t.gend ? p.a_scale[src_row(p, r)] : 0.0f;
+    } else if (i < RG_BM + RG_BN) {
+      const int n = t.n0 + i - RG_BM;
+      sc_col[i - RG_BM] = n < p.n ? p.w_scale[int64_t(t.g) * p.n + n] : 0.0f;
+    }
+  }
 
   const int wm = wave % WM;
   const int wn = wave / WM;
@@ -506,31 +525,117 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     // no LDS write may still be in flight when the workgroup ends
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   };
-  auto with_rows = [&](auto full_c) {
+  // fp8: one MFMA K step (16x16x128) takes 128 bytes of each row, ring
+  // stages 2u and 2u + 1; lane group g holds bytes [32 g, 32 g + 32), i.e.
+  // chunks 2 (g & 1) and 2 (g & 1) + 1 of stage 2u + (g >> 1).  Steps use the
+  // slot pairs {0, 1} and {2, 3} in turn: the pair of step u + 1 is fetched
+  // during step u.  A stage past the end of K (K / 64 odd) is zero-filled in
+  // LDS, so the last step adds exact zeros.
+  auto zero_fill = [&](char* buf) {
+#pragma unroll
+    for (int q = 0; q < DMA_PER_WAVE; ++q)
+      *reinterpret_cast<i32x4_t*>(buf + (wave + NW * q) * 1024 + lane * 16) = i32x4_t{0, 0, 0, 0};
+  };
+  auto fill = [&](int s, char* buf) {
+    if (s < nk)
+      dma(s, buf);
+    else
+      zero_fill(buf);
+  };
+  auto k_loop_fp8 = [&](auto fmv_c, auto full_c) {
+    constexpr int FMV = decltype(fmv_c)::value;
+    constexpr bool FULL_N = decltype(full_c)::value;
+    const int c0 = 2 * (lgrp & 1);
+    const int o0 = lrow * RG_ROWB + ((c0 ^ rg_swizzle(lrow)) * 16);
+    const int o1 = lrow * RG_ROWB + (((c0 + 1) ^ rg_swizzle(lrow)) * 16);
+    auto frag = [&](const char* p8) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(p8 + o0);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(p8 + o1);
+      i32x8_t r;
+      r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+      r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+      return r;
+    };
+    const int nsteps = (nk + 1) / 2;
+    fill(0, ring);
+    fill(1, ring + RG_STAGE);
+    for (int u = 0; u < nsteps; ++u) {
+      // this wave's fills of stages 2u, 2u + 1 have landed and its reads of
+      // step u - 1 are done; after the barrier the same holds for all waves
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+      block_sync_lds();
+      char* nxt = ring + ((u + 1) & 1) * 2 * RG_STAGE;
+      if (u + 1 < nsteps) {
+        fill(2 * u + 2, nxt);
+        fill(2 * u + 3, nxt + RG_STAGE);
+      }
+      const char* cur = ring + (u & 1) * 2 * RG_STAGE + (lgrp >> 1) * RG_STAGE;
+      i32x8_t af[FM], bf[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        if (FULL_N || j < fn_valid) bf[j] = frag(cur + RG_ABYTES + (wn + WN * j) * 1024);
+#pragma unroll
+      for (int i = 0; i < FMV; ++i) af[i] = frag(cur + (wm + WM * i) * 1024);
+#pragma unroll
+      for (int i = 0; i < FMV; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(af[i], bf[j], acc[i][j]);
+    }
+    __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+  };
+
+  auto with_rows = [&](auto& loop, auto full_c) {
     using I = int;
     switch (fm_valid) {
-      case 8: k_loop(std::integral_constant<I, 8>{}, full_c); break;
-      case 7: k_loop(std::integral_constant<I, 7>{}, full_c); break;
-      case 6: k_loop(std::integral_constant<I, 6>{}, full_c); break;
-      case 5: k_loop(std::integral_constant<I, 5>{}, full_c); break;
-      case 4: k_loop(std::integral_constant<I, 4>{}, full_c); break;
-      case 3: k_loop(std::integral_constant<I, 3>{}, full_c); break;
-      case 2: k_loop(std::integral_constant<I, 2>{}, full_c); break;
-      case 1: k_loop(std::integral_constant<I, 1>{}, full_c); break;
-      default: k_loop(std::integral_constant<I, 0>{}, full_c); break;
+      case 8: loop(std::integral_constant<I, 8>{}, full_c); break;
+      case 7: loop(std::integral_constant<I, 7>{}, full_c); break;
+      case 6: loop(std::integral_constant<I, 6>{}, full_c); break;
+      case 5: loop(std::integral_constant<I, 5>{}, full_c); break;
+      case 4: loop(std::integral_constant<I, 4>{}, full_c); break;
+      case 3: loop(std::integral_constant<I, 3>{}, full_c); break;
+      case 2: loop(std::integral_constant<I, 2>{}, full_c); break;
+      case 1: loop(std::integral_constant<I, 1>{}, full_c); break;
+      default: loop(std::integral_constant<I, 0>{}, full_c); break;
     }
   };
-  if (full_n)
-    with_rows(std::true_type{});
+  auto run = [&](auto& loop) {
+    if (full_n)
+      with_rows(loop, std::true_type{});
+    else
+      with_rows(loop, std::false_type{});
+  };
+  if constexpr (KIND == K_FP8)
+    run(k_loop_fp8);
   else
-    with_rows(std::false_type{});
+    run(k_loop);
 
+  // Epilogue: the same arithmetic as store_block, fp8 scales from LDS.
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      store_block<KIND, EPI>(t, acc[i][j], t.m0 + (wm + WM * i) * 16 + lgrp * 4,
-                             t.n0 + (wn + WN * j) * 16 + lrow);
+    for (int j = 0; j < FN; ++j) {
+      const int rl = (wm + WM * i) * 16 + lgrp * 4;  // tile-local first row
+      const int cl = (wn + WN * j) * 16 + lrow;      // tile-local column
+      const int col = t.n0 + cl;
+      if (col >= p.n) continue;
+      const float sw = KIND == K_FP8 ? sc_col[cl] : 1.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t r = t.m0 + rl + q;
+        if (r >= t.gend) break;
+        float v = acc[i][j][q];
+        if (KIND == K_FP8) v = (v * sc_row[rl + q]) * sw;
+        if (EPI == EPI_RELU2) {
+          v = fmaxf(v, 0.0f);
+          v = v * v;
+        }
+        if (p.out_bf16)
+          static_cast<uint16_t*>(p.out)[r * p.n + col] = f32_to_bf16(v);
+        else
+          static_cast<float*>(p.out)[r * p.n + col] = v;
+      }
+    }
 }
 
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
@@ -592,6 +697,9 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
                       stream, t, p);
   }
   if constexpr (KIND == K_FP8) {
+    if (shape.bm == RG_BM && MOE_FP8_RING)
+      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES>, g, dim3(MOE_RING_WAVES * WAVE),
+                      stream, t, p);
     if (shape.bm == 256)
       return launch_k(gemm_kernel<KIND, 256, 256, 2, 4, EPI, 512, 32>, g, dim3(512), stream, t,
                       p);
