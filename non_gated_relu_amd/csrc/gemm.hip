@@ -476,7 +476,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     for (int i = 2 * q; i < 2 * q + 2; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        if (i < FMV && (FULL_N || j < fn_valid)) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
+        if (i < FMV && (FULL_N || j < fn_valid)) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
   };
 
   // Stage s lives in ring slot s & 3 and is fetched three stages ahead.  Its
@@ -580,7 +580,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       for (int i = 0; i < FMV; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(af[i], bf[j], acc[i][j]);
+          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
     }
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   };
@@ -610,32 +610,42 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   else
     run(k_loop);
 
-  // Epilogue: the same arithmetic as store_block, fp8 scales from LDS.
+  // Epilogue: the same arithmetic as store_block, fp8 scales from LDS.  The
+  // MFMAs take the weight fragment as their first operand, so a lane holds
+  // the transposed block: one row and four consecutive columns, written
+  // with one 8-byte (bf16) or 16-byte (fp32) store.
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int rl = (wm + WM * i) * 16 + lrow;  // tile-local row
+    const int64_t r = t.m0 + rl;
+    if (r >= t.gend) continue;
+    const float sa = KIND == K_FP8 ? sc_row[rl] : 1.0f;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int rl = (wm + WM * i) * 16 + lgrp * 4;  // tile-local first row
-      const int cl = (wn + WN * j) * 16 + lrow;      // tile-local column
+      const int cl = (wn + WN * j) * 16 + lgrp * 4;  // tile-local first column
       const int col = t.n0 + cl;
-      if (col >= p.n) continue;
-      const float sw = KIND == K_FP8 ? sc_col[cl] : 1.0f;
+      if (col >= p.n) continue;  // N is a multiple of 16: a block is all in or all out
+      float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t r = t.m0 + rl + q;
-        if (r >= t.gend) break;
-        float v = acc[i][j][q];
-        if (KIND == K_FP8) v = (v * sc_row[rl + q]) * sw;
+        v[q] = acc[i][j][q];
+        if (KIND == K_FP8) v[q] = (v[q] * sa) * sc_col[cl + q];
         if (EPI == EPI_RELU2) {
-          v = fmaxf(v, 0.0f);
-          v = v * v;
+          v[q] = fmaxf(v[q], 0.0f);
+          v[q] = v[q] * v[q];
         }
-        if (p.out_bf16)
-          static_cast<uint16_t*>(p.out)[r * p.n + col] = f32_to_bf16(v);
-        else
-          static_cast<float*>(p.out)[r * p.n + col] = v;
+      }
+      if (p.out_bf16) {
+        uint2 w;
+        w.x = f32_to_bf16(v[0]) | (uint32_t(f32_to_bf16(v[1])) << 16);
+        w.y = f32_to_bf16(v[2]) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + r * p.n + col) = w;
+      } else {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + r * p.n + col) =
+            f32x4_t{v[0], v[1], v[2], v[3]};
       }
     }
+  }
 }
 
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
