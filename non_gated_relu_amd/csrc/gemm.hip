@@ -697,6 +697,8 @@ template <int KIND, int EPI>
 hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
                            Timing t) {
   const dim3 g(grid);
+  if (shape.bm == 16 && shape.bn == 64)
+    return launch_k(gemm_kernel<KIND, 16, 64, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if (shape.bm == 16)
     return launch_k(gemm_kernel<KIND, 16, 128, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if (shape.bm == 64)
@@ -727,9 +729,11 @@ hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned gri
 
 }  // namespace
 
-GemmShape pick_gemm_shape(int kind, int64_t rows, int groups) {
+GemmShape pick_gemm_shape(int kind, int64_t rows, int groups, bool down) {
   const int64_t avg = groups > 0 ? rows / groups : rows;
-  if (avg <= 24) return GemmShape{16, 128};
+  // decode: a weight stream; the up projection (K = hidden) streams best in
+  // 64-wide tiles, the down projection (K = inter) in 128-wide ones
+  if (avg <= 24) return GemmShape{16, down ? 128 : 64};
   if (avg <= 80) return GemmShape{64, 128};
   if (avg < 128 || kind == K_F32) return GemmShape{128, 128};
   return GemmShape{256, 256};

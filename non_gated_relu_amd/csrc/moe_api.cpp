@@ -118,13 +118,15 @@ struct Mlp {
 // Shape and tile bound of a launch over `main` (+ `extra_rows` of a second
 // single-group problem).
 struct FfnPlan {
-  GemmShape shape;
+  GemmShape shape;       // up projection
+  GemmShape down_shape;  // down projection (same BM)
   int64_t mtiles;
 };
 
 FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats, int64_t extra_rows) {
   FfnPlan f;
-  f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats);
+  f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats, false);
+  f.down_shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats, true);
   f.mtiles = max_mtiles(rows, n_mats, f.shape.bm) +
              (extra_rows > 0 ? (extra_rows + f.shape.bm - 1) / f.shape.bm : 0);
   return f;
@@ -200,13 +202,12 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
     QuantArgs q{m.a, m.aq, m.as, m.a_rows, hidden, 1};
     if (launch_quant(q, s, tm.qa) != hipSuccess) return MOE_ERR_HIP;
   }
-  const int bn = f.shape.bn;
   GemmArgs up{};
   up.prob[0] = up_problem(m, hidden);
   if (extra) up.prob[1] = up_problem(*extra, hidden);
   up.sched = sched;
   up.n_groups = m.n_mats;
-  up.n_tiles = (std::max(m.inter, extra ? extra->inter : 0) + bn - 1) / bn;
+  up.n_tiles = (std::max(m.inter, extra ? extra->inter : 0) + f.shape.bn - 1) / f.shape.bn;
   if (launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s, tm.up) != hipSuccess)
     return MOE_ERR_HIP;
   if (kind == K_FP8) {
@@ -218,8 +219,8 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   if (extra) dn.prob[1] = down_problem(*extra, hidden);
   dn.sched = sched;
   dn.n_groups = m.n_mats;
-  dn.n_tiles = (hidden + bn - 1) / bn;
-  if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down) != hipSuccess)
+  dn.n_tiles = (hidden + f.down_shape.bn - 1) / f.down_shape.bn;
+  if (launch_gemm(dn, kind, EPI_PLAIN, f.down_shape, f.mtiles, s, tm.down) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
