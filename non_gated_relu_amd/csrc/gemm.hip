@@ -362,7 +362,7 @@ __device__ __forceinline__ void block_sync_lds() {
 // NW waves in a 2 x (NW / 2) grid; wave (wm, wn) owns the 16-row blocks
 // wm + 2 i and the 16-column blocks wn + (NW / 2) j of the tile, dealt
 // round-robin so that partial tiles leave every SIMD about the same work.
-template <int KIND, int EPI, int NW>
+template <int KIND, int EPI, int NW, int RING>
 __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   constexpr int WM = 2, WN = NW / 2;
   constexpr int FM = RG_BM / WM / 16;  // 8
@@ -371,7 +371,11 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   constexpr int QUARTERS = 4;
   static_assert(KIND == K_BF16 || KIND == K_FP8, "the ring kernel takes bf16 or fp8 operands");
   static_assert(DMA_PER_WAVE % QUARTERS == 0 && FN % QUARTERS == 0, "quarter split");
-  __shared__ __attribute__((aligned(1024))) char ring[4 * RG_STAGE];
+  // (a fifth bf16 slot, 160 KB in all, measured 2-3% slower)
+  static_assert(KIND == K_BF16 ? (RING == 4 || RING == 5) : RING == 4, "ring depth");
+  // the ring, then (fp8) the tile's row and column scales
+  constexpr int SCALE_BYTES = KIND == K_FP8 ? 4 * (RG_BM + RG_BN) : 0;
+  __shared__ __attribute__((aligned(1024))) char ring[RING * RG_STAGE + SCALE_BYTES];
 
   Tile t;
   const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
@@ -419,8 +423,8 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   // fp8: the tile's row scales (activation rows) and column scales (weight
   // rows), staged once in LDS for the epilogue; the K loop's first barrier
   // makes them visible.
-  __shared__ float sc_row[KIND == K_FP8 ? RG_BM : 1];
-  __shared__ float sc_col[KIND == K_FP8 ? RG_BN : 1];
+  float* sc_row = reinterpret_cast<float*>(ring + RING * RG_STAGE);
+  float* sc_col = sc_row + RG_BM;
   if constexpr (KIND == K_FP8) {
     const int i = threadIdx.x;
     if (i < RG_BM) {
@@ -479,29 +483,30 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
         if (i < FMV && (FULL_N || j < fn_valid)) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
   };
 
-  // Stage s lives in ring slot s & 3 and is fetched three stages ahead.  Its
-  // fragments are read from LDS one stage ahead, during the MFMAs of stage
-  // s - 1, so LDS latency hides behind MFMA work.  At the top of step s the
-  // wave waits for its DMA of stage s+1 (stage s+2 may still fly) and for its
-  // fragment reads of stage s, issued a whole step earlier (so that nothing
-  // waits on the reads it issues next); the barrier then makes stage s+1
-  // visible to all waves and ensures slot (s + 3) & 3, read for stage s-1
-  // during step s-2, is free.  The step's DMA and LDS reads are spread
-  // between its MFMAs, a quarter at a time, so that no burst of memory
-  // instructions holds up MFMA issue.
-  constexpr int WAIT_NEXT = waitcnt_imm(DMA_PER_WAVE, 0);
-  constexpr int WAIT_FIRST = waitcnt_imm(2 * DMA_PER_WAVE, 15);
+  // Stage s lives in ring slot s % RING and is fetched RING - 1 stages ahead.
+  // Its fragments are read from LDS one stage ahead, during the MFMAs of
+  // stage s - 1, so LDS latency hides behind MFMA work.  At the top of step s
+  // the wave waits for its DMA of stage s+1 (stages s+2 .. s+RING-2 may still
+  // fly) and for its fragment reads of stage s, issued a whole step earlier
+  // (so that nothing waits on the reads it issues next); the barrier then
+  // makes stage s+1 visible to all waves and ensures slot (s - 1) % RING, read
+  // for stage s-1 during step s-2, is free for stage s + RING - 1.  The
+  // step's DMA and LDS reads are spread between its MFMAs, a quarter at a
+  // time, so that no burst of memory instructions holds up MFMA issue.
+  constexpr int WAIT_NEXT = waitcnt_imm((RING - 3) * DMA_PER_WAVE, 0);
+  constexpr int WAIT_FIRST = waitcnt_imm((RING - 2) * DMA_PER_WAVE, 15);
+  auto slot = [&](int s) { return ring + (s % RING) * RG_STAGE; };
   auto step = [&](int s, const i32x4_t (&ca)[FM], const i32x4_t (&cb)[FN], i32x4_t (&na)[FM],
                   i32x4_t (&nb)[FN], auto fmv_c, auto full_c) {
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
     block_sync_lds();
-    char* dbuf = ring + ((s + 3) & 3) * RG_STAGE;
-    const char* nbuf = ring + ((s + 1) & 3) * RG_STAGE;
+    char* dbuf = slot(s + RING - 1);
+    const char* nbuf = slot(s + 1);
 #pragma unroll
     for (int q = 0; q < QUARTERS; ++q) {
 #pragma unroll
       for (int d = q * (DMA_PER_WAVE / QUARTERS); d < (q + 1) * (DMA_PER_WAVE / QUARTERS); ++d)
-        dma_one(d, s + 3, dbuf);
+        dma_one(d, s + RING - 1, dbuf);
       load_quarter(q, nbuf, na, nb, fmv_c, full_c);
       __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
       mma_quarter(q, ca, cb, fmv_c, full_c);
@@ -510,9 +515,8 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   };
   auto k_loop = [&](auto fmv_c, auto full_c) {
     i32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
-    dma(0, ring);
-    dma(1, ring + RG_STAGE);
-    dma(2, ring + 2 * RG_STAGE);
+#pragma unroll
+    for (int s = 0; s < RING - 1; ++s) dma(s, ring + s * RG_STAGE);
     __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
     block_sync_lds();
 #pragma unroll
@@ -525,6 +529,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     // no LDS write may still be in flight when the workgroup ends
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   };
+
   // fp8: one MFMA K step (16x16x128) takes 128 bytes of each row, ring
   // stages 2u and 2u + 1; lane group g holds bytes [32 g, 32 g + 32), i.e.
   // chunks 2 (g & 1) and 2 (g & 1) + 1 of stage 2u + (g >> 1).  Steps use the
@@ -705,12 +710,12 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
     return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if constexpr (KIND == K_BF16) {
     if (shape.bm == RG_BM)
-      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES>, g, dim3(MOE_RING_WAVES * WAVE),
-                      stream, t, p);
+      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES, 4>, g,
+                      dim3(MOE_RING_WAVES * WAVE), stream, t, p);
   }
   if constexpr (KIND == K_FP8) {
     if (shape.bm == RG_BM && MOE_FP8_RING)
-      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES>, g, dim3(MOE_RING_WAVES * WAVE),
+      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES, 4>, g, dim3(MOE_RING_WAVES * WAVE),
                       stream, t, p);
     if (shape.bm == 256)
       return launch_k(gemm_kernel<KIND, 256, 256, 2, 4, EPI, 512, 32>, g, dim3(512), stream, t,

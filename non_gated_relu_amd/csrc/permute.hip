@@ -308,35 +308,49 @@ __global__ __launch_bounds__(PM_THREADS) void schedule_kernel(ScheduleArgs p) {
 // y[t] = sum_j w[t,j] * y_perm[slot_pos[t*k+j]] (+ shared[t]), fp32, rounded once.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
-  const int64_t t = blockIdx.x;
-  const int k = p.top_k;
+  // one float4 of one token per thread, over a flat grid of tokens x columns
   const int d4 = p.hidden / 4;
-  __shared__ int32_t pos[64];
-  __shared__ float w[64];
-  if (threadIdx.x < k) {
-    pos[threadIdx.x] = p.slot_pos[t * k + threadIdx.x];
-    w[threadIdx.x] = p.topk_w[t * k + threadIdx.x];
+  const int64_t idx = int64_t(blockIdx.x) * PM_THREADS + threadIdx.x;
+  const int64_t t = idx / d4;
+  if (t >= p.tokens) return;
+  const int c = static_cast<int>(idx - t * d4);
+  const int k = p.top_k;
+  const int32_t* pos = p.slot_pos + t * k;
+  const float* wt = p.topk_w + t * k;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // the (read-once) rows of up to 8 slots are fetched together, then summed
+  // in ascending j
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4_t v[8];
+    float w[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < k) {
+        w[jj] = wt[j0 + jj];
+        v[jj] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4_t*>(p.y_perm + int64_t(pos[j0 + jj]) * p.hidden) + c);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj < k) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w[jj], v[jj][q], acc[q]);
+      }
+    }
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < d4; c += PM_THREADS) {
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.y_perm + int64_t(pos[j]) * p.hidden + c * 4);
+  if (p.shared) {
+    const f32x4_t sv =
+        __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p.shared + t * p.hidden) + c);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(w[j], v[q], acc[q]);
-    }
-    if (p.shared) {
-      const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(p.shared + t * p.hidden + c * 4);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = acc[q] + sv[q];
-    }
-    if (BF16_OUT) {
-      uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);
-      uint32_t hi = f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16);
-      reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.hidden)[c] = make_uint2(lo, hi);
-    } else {
-      reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.hidden)[c] = acc;
-    }
+    for (int q = 0; q < 4; ++q) acc[q] = acc[q] + sv[q];
+  }
+  if (BF16_OUT) {
+    uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+    uint32_t hi = f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.hidden)[c] = make_uint2(lo, hi);
+  } else {
+    reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.hidden)[c] = acc;
   }
 }
 
@@ -370,7 +384,9 @@ hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t) 
 }
 
 hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream, Timing t) {
-  dim3 grid(static_cast<unsigned>(p.tokens));
+  const int64_t threads = p.tokens * (p.hidden / 4);
+  if (threads <= 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((threads + PM_THREADS - 1) / PM_THREADS));
   if (bf16_out) return launch_k(combine_kernel<true>, grid, dim3(PM_THREADS), stream, t, p);
   return launch_k(combine_kernel<false>, grid, dim3(PM_THREADS), stream, t, p);
 }
