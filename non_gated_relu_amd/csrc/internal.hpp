@@ -50,8 +50,10 @@ struct ScheduleSpec {
 // How the router gets its logits (route.hip).
 enum RouteMode : int { ROUTE_ONE_KERNEL = 0, ROUTE_WAVES = 1, ROUTE_GEMM = 2 };
 
-// Routing slots per permute workgroup (one workgroup does it all up to here).
-constexpr int PM_CHUNK = 4096;
+// Routing slots the single-workgroup permute handles; beyond, the slots are
+// split into chunks of PM_CHUNK, one workgroup each.
+constexpr int PM_SMALL_MAX = 4096;
+constexpr int PM_CHUNK = 1024;
 
 struct PermuteArgs {
   const int32_t* topk_idx;  // [slots]
@@ -61,7 +63,7 @@ struct PermuteArgs {
   int32_t* slot_pos;        // [slots]
   int32_t* block_counts;    // [n_chunks, E] workspace
   int64_t slots;
-  int n_chunks;             // ceil(slots / PM_CHUNK)
+  int n_chunks;             // 1 (single workgroup), else ceil(slots / PM_CHUNK)
   int n_experts;
   ScheduleSpec sched;       // optional: schedule of the expert GEMMs
 };

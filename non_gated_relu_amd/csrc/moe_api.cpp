@@ -12,7 +12,7 @@
 //
 // Launch sequence of moe_forward (one stream, no host synchronisation):
 //   route (1 kernel, or 2 for few tokens) -> permute (1 kernel for at most
-//   PM_CHUNK slots, else 3; it also writes the GEMM tile schedule) ->
+//   PM_SMALL_MAX slots, else 3; it also writes the GEMM tile schedule) ->
 //   [fp8: quantise x] -> up GEMM + relu^2 -> [fp8: quantise h] -> down GEMM
 //   -> combine.  When the shared expert's weights have the routed experts'
 //   type it rides in the same two GEMM launches as one extra group; with fp8
@@ -245,6 +245,7 @@ struct Forward {
 };
 
 int permute_chunks(int64_t slots) {
+  if (slots <= PM_SMALL_MAX) return 1;
   return static_cast<int>((slots + PM_CHUNK - 1) / PM_CHUNK);
 }
 

@@ -29,13 +29,14 @@ __device__ __forceinline__ uint64_t match_key(uint32_t key) {
   return m;
 }
 
-// Copies the expert ids of slots [s0, s0 + n), n <= PM_CHUNK, into LDS.  All
+// Copies the expert ids of slots [s0, s0 + n), n <= MAXN, into LDS.  All
 // loads are issued before the first store, so the chunk costs one memory
 // round trip.  Ids outside [0, E) are clamped so every later write stays
 // inside its array.  Ends with a barrier.
+template <int MAXN>
 __device__ void stage_ids(const int32_t* __restrict__ idx, int64_t s0, int n, int E,
                           int32_t* ids) {
-  constexpr int PER = PM_CHUNK / PM_THREADS;
+  constexpr int PER = MAXN / PM_THREADS;
   int32_t v[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -178,11 +179,11 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p
   __shared__ int32_t tmp[PM_THREADS];
   __shared__ int32_t carry;
   const int E = p.n_experts;
-  __shared__ int32_t ids[PM_CHUNK];
+  __shared__ int32_t ids[PM_SMALL_MAX];
   const int n = static_cast<int>(p.slots);
   for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
   for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
-  stage_ids(p.topk_idx, 0, n, E, ids);
+  stage_ids<PM_SMALL_MAX>(p.topk_idx, 0, n, E, ids);
   for (int i = threadIdx.x; i < n; i += PM_THREADS) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PM_THREADS) {
@@ -212,45 +213,71 @@ __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(PermuteArgs p)
   for (int e = threadIdx.x; e < E; e += PM_THREADS) cnt[e] = 0;
   const int64_t s0 = int64_t(blockIdx.x) * PM_CHUNK;
   const int n = static_cast<int>(min<int64_t>(PM_CHUNK, p.slots - s0));
-  stage_ids(p.topk_idx, s0, n, E, ids);
+  stage_ids<PM_CHUNK>(p.topk_idx, s0, n, E, ids);
   for (int i = threadIdx.x; i < n; i += PM_THREADS) atomicAdd(&cnt[ids[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PM_THREADS) p.block_counts[blockIdx.x * E + e] = cnt[e];
 }
 
 // Pass 2 (one workgroup): per-expert totals, offsets, each chunk's base, and
-// the GEMM schedule.
+// the GEMM schedule.  The chunk counts are scanned in LDS when they fit
+// (n_chunks * E <= PM_SCAN_LDS), with coalesced loads and stores; otherwise
+// each expert's column is walked in global memory.
+constexpr int PM_SCAN_LDS = 16384;
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p) {
   __shared__ int32_t off[1024];
   __shared__ int32_t cnt[1024];
   __shared__ int32_t tiles[1024];
   __shared__ int32_t tmp[PM_THREADS];
+  __shared__ int32_t bc[PM_SCAN_LDS];
   __shared__ int32_t carry;
   const int E = p.n_experts;
-  constexpr int B = 8;  // chunk counts loaded per batch
-  for (int e = threadIdx.x; e < E; e += PM_THREADS) {
-    int32_t total = 0;
-    for (int b0 = 0; b0 < p.n_chunks; b0 += B) {
-      int32_t v[B];
+  const int nb = p.n_chunks * E;
+  const bool in_lds = nb <= PM_SCAN_LDS;
+  if (in_lds) {
+    for (int i = threadIdx.x; i < nb; i += PM_THREADS) bc[i] = p.block_counts[i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+      int32_t total = 0;
+      for (int b = 0; b < p.n_chunks; ++b) {
+        const int32_t v = bc[b * E + e];
+        bc[b * E + e] = total;  // the chunk's base inside expert e
+        total += v;
+      }
+      p.expert_counts[e] = total;
+      off[e] = total;
+      cnt[e] = total;
+    }
+  } else {
+    constexpr int B = 8;  // chunk counts loaded per batch
+    for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+      int32_t total = 0;
+      for (int b0 = 0; b0 < p.n_chunks; b0 += B) {
+        int32_t v[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) v[u] = b0 + u < p.n_chunks ? p.block_counts[(b0 + u) * E + e] : 0;
+        for (int u = 0; u < B; ++u)
+          v[u] = b0 + u < p.n_chunks ? p.block_counts[(b0 + u) * E + e] : 0;
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        if (b0 + u < p.n_chunks) {
-          p.block_counts[(b0 + u) * E + e] = total;  // the chunk's base inside expert e
-          total += v[u];
+        for (int u = 0; u < B; ++u) {
+          if (b0 + u < p.n_chunks) {
+            p.block_counts[(b0 + u) * E + e] = total;
+            total += v[u];
+          }
         }
       }
+      p.expert_counts[e] = total;
+      off[e] = total;
+      cnt[e] = total;
     }
-    p.expert_counts[e] = total;
-    off[e] = total;
-    cnt[e] = total;
   }
   __syncthreads();
   block_exclusive_scan(off, E, tmp);
-  for (int e = threadIdx.x; e < E; e += PM_THREADS) {
-    p.expert_offsets[e] = off[e];
-    for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];
+  for (int e = threadIdx.x; e < E; e += PM_THREADS) p.expert_offsets[e] = off[e];
+  if (in_lds) {
+    for (int i = threadIdx.x; i < nb; i += PM_THREADS) p.block_counts[i] = bc[i] + off[i % E];
+  } else {
+    for (int e = threadIdx.x; e < E; e += PM_THREADS)
+      for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];
   }
   if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
   if (p.sched.sched)
@@ -272,7 +299,7 @@ __global__ __launch_bounds__(PM_THREADS) void permute_place_kernel(PermuteArgs p
   for (int i = threadIdx.x; i < PM_WAVES * E; i += PM_THREADS) wc[i] = 0;
   const int64_t s0 = int64_t(blockIdx.x) * PM_CHUNK;
   const int n = static_cast<int>(min<int64_t>(PM_CHUNK, p.slots - s0));
-  stage_ids(p.topk_idx, s0, n, E, ids);
+  stage_ids<PM_CHUNK>(p.topk_idx, s0, n, E, ids);
   place_chunk(ids, s0, n, E, run, wc, p.sorted_slot, p.slot_pos);
 }
 

@@ -280,3 +280,31 @@ def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
         allow = fp8_flips.row_allowance(inp["x"], src.cpu().numpy(), mats, inp["w_up"],
                                         inp["w_up_scale"], inp["w_down"], inp["w_down_scale"])
     assert_close_rms(to_f64(big), ref, f"{wl.name} expert_ffn 256-row tiles", row_allow=allow)
+
+
+@pytest.mark.parametrize("T,k,E,skew", [(1500, 6, 128, False), (4097, 6, 128, True),
+                                        (16384, 6, 128, True), (3000, 3, 16, False)])
+def test_permute_many_chunks_matches_the_oracle(T, k, E, skew):
+    """The multi-workgroup permute (slots beyond one workgroup's share) gives
+    exactly the oracle's stable grouping, counts and offsets."""
+    print(f"case T={T} k={k} E={E} skew={skew}", flush=True)
+    rng = np.random.default_rng(T + k + E)
+    if skew:  # two thirds of the slots on 8 experts, some experts empty
+        hot = rng.choice(E, size=8, replace=False)
+        p = np.full(E, 1.0 / (3 * (E - 8)))
+        p[hot] = 2.0 / (3 * 8)
+        p[rng.choice(np.setdiff1d(np.arange(E), hot), size=E // 4, replace=False)] = 0.0
+        p /= p.sum()
+    else:
+        p = np.full(E, 1.0 / E)
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    idx.sort(axis=1)
+    cfg = binding.config_from(dataclasses.replace(WORKLOADS["decode-bf16-T32"], n_experts=E,
+                                                  n_group=1 if E == 16 else 8, top_k=k))
+    perm = binding.permute(cfg, torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    counts, offsets, sorted_slot, slot_pos = oracle.permute(idx, E)
+    np.testing.assert_array_equal(perm["counts"].cpu().numpy(), counts)
+    np.testing.assert_array_equal(perm["offsets"].cpu().numpy(), offsets)
+    np.testing.assert_array_equal(perm["sorted_slot"].cpu().numpy(), sorted_slot)
+    np.testing.assert_array_equal(perm["slot_pos"].cpu().numpy(), slot_pos)
