@@ -653,7 +653,110 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   }
 }
 
+// ---------------------------------------------------------- stream kernel
+//
+// Thin (16-row) tiles of bf16 GEMMs that stream their weights: the expert
+// MLPs at decode, where an expert sees a handful of rows, and the router's
+// logits.  There is little MFMA work per byte, so what matters is how many
+// bytes each CU keeps in flight: K moves in 64-byte row slices (the ring
+// kernel's swizzled 1 KB block layout) through a ring of SK_RING LDS stages
+// filled by global_load_lds_dwordx4 SK_RING - 1 stages ahead, with no
+// staging registers; at 9 KB a stage that is about 125 KB in flight per CU.
+// Same MFMA and per-lane K bytes as gemm_kernel, so the same results.
+constexpr int SK_BM = 16;
+constexpr int SK_RING = 8;
+
+template <int KIND, int BN, int EPI>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
+  static_assert(KIND == K_BF16, "the stream kernel takes bf16 operands");
+  constexpr int NBLK = 1 + BN / 16;          // 1 KB blocks per stage: A, then B
+  constexpr int STAGE = NBLK * 1024;
+  constexpr int FN = BN / 64;                // column fragments per wave (4 waves along N)
+  constexpr int MAXQ = (NBLK + 3) / 4;       // blocks one wave fetches per stage, at most
+  __shared__ __attribute__((aligned(1024))) char ring[SK_RING * STAGE];
+
+  Tile t;
+  if (!locate_tile<SK_BM, BN>(pa, t, blockIdx.x)) return;
+  const GemmProblem& p = t.p;
+  const int wave = threadIdx.x / WAVE;
+  const int lane = lane_id();
+  const int64_t kbytes = int64_t(p.k) * 2;
+  const int nk = static_cast<int>(kbytes / RG_ROWB);  // the host guarantees K bytes % 64 == 0
+
+  // wave w fetches blocks w, w + 4, w + 8 (< NBLK); rows past the group end
+  // or past N re-read the last valid row (their outputs are never stored)
+  const int r_in = lane >> 2;
+  const int chunk = (lane & 3) ^ rg_swizzle(r_in);
+  const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
+  const char* src[MAXQ];
+#pragma unroll
+  for (int q = 0; q < MAXQ; ++q) {
+    const int blk = min(wave + 4 * q, NBLK - 1);
+    if (blk == 0) {
+      const int64_t r = min<int64_t>(t.m0 + r_in, t.gend - 1);
+      src[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
+    } else {
+      const int n = min(t.n0 + (blk - 1) * 16 + r_in, p.n - 1);
+      src[q] = wbase + int64_t(n) * kbytes + chunk * 16;
+    }
+  }
+  const int mine = (NBLK - wave + 3) / 4;  // blocks this wave fetches per stage
+  auto dma = [&](int s, char* buf) {
+    const int64_t kb = int64_t(min(s, nk - 1)) * RG_ROWB;  // past the end: harmless re-read
+#pragma unroll
+    for (int q = 0; q < MAXQ; ++q) {
+      if (q < mine) {
+        const void* from = src[q] + kb;
+        __builtin_amdgcn_global_load_lds(from, MOE_LDS_PTR(buf + (wave + 4 * q) * 1024), 16, 0,
+                                         0);
+      }
+    }
+  };
+  // wait until this wave's DMA of the oldest stage in flight has landed, the
+  // SK_RING - 2 younger stages may still fly; and its LDS reads are done
+  auto wait_oldest = [&]() {
+    if (mine >= 3)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((SK_RING - 2) * 3, 0));
+    else if (mine == 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm((SK_RING - 2) * 2, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(SK_RING - 2, 0));
+  };
+
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int lofs = lrow * RG_ROWB + ((lgrp ^ rg_swizzle(lrow)) * 16);
+  f32x4_t acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int s = 0; s < SK_RING - 1; ++s) dma(s, ring + s * STAGE);
+  for (int s = 0; s < nk; ++s) {
+    wait_oldest();
+    block_sync_lds();  // stage s is in LDS for all waves; slot (s - 1) % SK_RING is free
+    dma(s + SK_RING - 1, ring + ((s + SK_RING - 1) % SK_RING) * STAGE);
+    const char* buf = ring + (s % SK_RING) * STAGE;
+    const i32x4_t af = *reinterpret_cast<const i32x4_t*>(buf + lofs);
+    i32x4_t bf[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      bf[j] = *reinterpret_cast<const i32x4_t*>(buf + (1 + wave * FN + j) * 1024 + lofs);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[j] = mfma_bf16(af, bf[j], acc[j]);
+  }
+  // no LDS write may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(WAIT_VM0);
+
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    store_block<KIND, EPI>(t, acc[j], t.m0 + lgrp * 4, t.n0 + (wave * FN + j) * 16 + lrow);
+}
+
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
+// Rows up to QV_MAX * 256 columns are read once into registers (all loads in
+// flight together); longer rows are read twice.
+constexpr int QV_MAX = 12;
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
   const int64_t row = int64_t(blockIdx.x) * 4 + threadIdx.x / WAVE;
   if (row >= p.rows) return;
@@ -661,39 +764,70 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
   const int cols = p.cols;
   auto ld4 = [&](int c, float* v) {
     if (p.in_bf16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.in) +
-                                                      row * cols + c);
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      const u32x2_t u = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p.in) + row * cols + c));
       v[0] = __uint_as_float(u.x << 16);
       v[1] = __uint_as_float(u.x & 0xFFFF0000u);
       v[2] = __uint_as_float(u.y << 16);
       v[3] = __uint_as_float(u.y & 0xFFFF0000u);
     } else {
-      const f32x4_t f = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.in) +
-                                                         row * cols + c);
+      const f32x4_t f = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.in) + row * cols + c));
       v[0] = f[0];
       v[1] = f[1];
       v[2] = f[2];
       v[3] = f[3];
     }
   };
-  float amax = 0.0f;
-  for (int c = lane * 4; c < cols; c += WAVE * 4) {
-    float v[4];
-    ld4(c, v);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(v[q]));
-  }
-#pragma unroll
-  for (int off = WAVE / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float s = amax / 448.0f;
-  if (s == 0.0f) s = 1.0f;
-  for (int c = lane * 4; c < cols; c += WAVE * 4) {
-    float v[4];
-    ld4(c, v);
+  auto quant4 = [&](const float* v, float s) {
     uint32_t w = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) w |= f32_to_e4m3(v[q] / s) << (8 * q);
-    *reinterpret_cast<uint32_t*>(p.q + row * cols + c) = w;
+    return w;
+  };
+  auto row_scale = [&](float amax) {
+#pragma unroll
+    for (int off = WAVE / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    const float s = amax / 448.0f;
+    return s == 0.0f ? 1.0f : s;
+  };
+  float s;
+  if (cols <= QV_MAX * WAVE * 4) {
+    float v[QV_MAX][4];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < QV_MAX; ++i) {
+      const int c = (i * WAVE + lane) * 4;
+      if (c < cols) ld4(c, v[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < QV_MAX; ++i) {
+      const int c = (i * WAVE + lane) * 4;
+      if (c < cols)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(v[i][q]));
+    }
+    s = row_scale(amax);
+#pragma unroll
+    for (int i = 0; i < QV_MAX; ++i) {
+      const int c = (i * WAVE + lane) * 4;
+      if (c < cols) *reinterpret_cast<uint32_t*>(p.q + row * cols + c) = quant4(v[i], s);
+    }
+  } else {
+    float amax = 0.0f;
+    for (int c = lane * 4; c < cols; c += WAVE * 4) {
+      float v[4];
+      ld4(c, v);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    }
+    s = row_scale(amax);
+    for (int c = lane * 4; c < cols; c += WAVE * 4) {
+      float v[4];
+      ld4(c, v);
+      *reinterpret_cast<uint32_t*>(p.q + row * cols + c) = quant4(v, s);
+    }
   }
   if (lane == 0) p.scale[row] = s;
 }
@@ -702,6 +836,10 @@ template <int KIND, int EPI>
 hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
                            Timing t) {
   const dim3 g(grid);
+  if constexpr (KIND == K_BF16) {
+    if (shape.stream && shape.bm == SK_BM && shape.bn == 128)
+      return launch_k(gemm_stream_kernel<KIND, 128, EPI>, g, dim3(256), stream, t, p);
+  }
   if (shape.bm == 16 && shape.bn == 64)
     return launch_k(gemm_kernel<KIND, 16, 64, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if (shape.bm == 16)

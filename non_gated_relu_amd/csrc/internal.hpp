@@ -131,9 +131,14 @@ struct QuantArgs {
   int in_bf16;
 };
 
-// Tile shape of a grouped GEMM launch.
+// Tile shape of a grouped GEMM launch.  `stream` asks for the DMA-ring
+// kernel of thin tiles (bf16, bm = 16), which keeps more bytes in flight but
+// reads rows in 64-byte slices: it wins for the router's logits, where every
+// tile re-reads the small gate matrix from L2, and loses to the register-
+// staged kernel's 128-byte reads when the tiles stream weights from HBM.
 struct GemmShape {
   int bm, bn;
+  bool stream = false;
 };
 
 // ROUTE_ONE_KERNEL computes logits and selects in one kernel; the other modes

@@ -145,12 +145,11 @@ hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stre
     q.index_div = 1;
     g.sched = nullptr;
     g.n_groups = 1;
-    // The gate matrix is small (E x d) and every M tile streams all of it from
-    // L2, so tiles are as tall as keeps some 256+ workgroups in flight: short
-    // tiles at a few thousand tokens, taller ones beyond.  Every shape gives
-    // the same logits (one MFMA chain per element, K ascending).
-    const int bm = p.tokens <= 4096 ? 16 : (p.tokens <= 16384 ? 64 : 128);
-    const GemmShape shape{bm, 128};
+    // Every M tile streams the whole (small, E x d) gate matrix from L2: thin
+    // tiles through the DMA-ring kernel keep the most of it in flight up to
+    // some 8k tokens; beyond, 64-row tiles re-read it less often.  Every
+    // shape gives the same logits (one MFMA chain per element, K ascending).
+    const GemmShape shape = p.tokens <= 8192 ? GemmShape{16, 128, true} : GemmShape{64, 128};
     g.n_tiles = (p.n_experts + shape.bn - 1) / shape.bn;
     const int64_t mtiles = (p.tokens + shape.bm - 1) / shape.bm;
     e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, stream, first);
