@@ -24,10 +24,14 @@ weights, so every tensor is a Gaussian draw:
   bf16 workloads round them to bf16 (round to nearest even);
 * rows of x for T tokens are a prefix of the rows for any larger T.
 
-The low-precision workload stores the routed expert weights as OCP fp8 e4m3
-codes with one fp32 scale per output channel (amax / 448), which is how those
-weights arrive at the layer; quantising the layer's activations is the layer's
-own work and does not happen here.
+The low-precision workloads store the routed expert weights as they arrive at
+the layer: OCP fp8 e4m3 codes with one fp32 scale per output channel
+(amax / 448), or 4-bit OCP MXFP4 (e2m1 codes, two per byte with the lower
+index in the low nibble, and one E8M0 power-of-two scale per block of 32
+along the input dimension, chosen as the OCP MX spec's conversion does:
+shared exponent floor(log2 amax) - 2, codes rounded to nearest even and
+saturated at 6).  Quantising the layer's activations is the layer's own work
+and does not happen here.
 """
 
 from __future__ import annotations
@@ -37,7 +41,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-F32, BF16, FP8 = "f32", "bf16", "fp8"
+F32, BF16, FP8, FP4 = "f32", "bf16", "fp8", "fp4"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -79,6 +83,9 @@ WORKLOADS = {
                                  bias_boost=(0, 4, 8, 12, 64, 68, 72, 76), bias_boost_value=2.0,
                                  **_NEMOTRON),
     "fp8-T8192": Workload("fp8-T8192", 8192, act_dtype=BF16, expert_dtype=FP8, **_NEMOTRON),
+    # routed experts in 4-bit MXFP4 (W4A16: activations and h stay bf16)
+    "decode-fp4-T32": Workload("decode-fp4-T32", 32, act_dtype=BF16, expert_dtype=FP4,
+                               **_NEMOTRON),
 }
 
 
@@ -124,6 +131,36 @@ def quantize_weight_rows_e4m3(w: np.ndarray):
     return q, scale
 
 
+_E2M1_MIDS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def _e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """Values -> OCP e2m1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and signs), nearest,
+    ties to the even code, magnitudes above 6 saturating to 6."""
+    v = np.asarray(v, dtype=np.float64)
+    mag = np.abs(v)
+    code = np.searchsorted(_E2M1_MIDS, mag, side="left")
+    tie = (code < 7) & (mag == _E2M1_MIDS[np.minimum(code, 6)])
+    code = np.where(tie & (code % 2 == 1), code + 1, code)
+    sign = ((v < 0) & (code != 0)).astype(np.int64) << 3
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_weight_rows_mxfp4(w: np.ndarray):
+    """[rows, cols] (cols % 32 == 0) -> (packed codes [rows, cols/2] uint8,
+    E8M0 block scales [rows, cols/32] uint8)."""
+    w = np.asarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    b = w.reshape(rows, cols // 32, 32).astype(np.float64)
+    amax = np.abs(b).max(axis=-1)
+    _, ex = np.frexp(amax)                      # amax = m 2^ex, m in [0.5, 1)
+    X = np.where(amax > 0, ex - 1 - 2, -127)    # floor(log2 amax) - emax(e2m1)
+    X = np.clip(X, -127, 127)
+    codes = _e2m1_codes(b / np.ldexp(1.0, X)[..., None]).reshape(rows, cols)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
 # ---------------------------------------------------------------------------
 
 def _draw(seed_seq, shape, std):
@@ -144,9 +181,11 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
 
     Keys: x [T,d], w_gate [E,d], e_bias [E] f32, w_up [E,I,d], w_down [E,d,I],
     ws_up [Is,d], ws_down [d,Is]; plus w_up_scale [E,I] and w_down_scale [E,d]
-    (fp32, or None) when the routed weights are fp8.  bf16 tensors are uint16
-    bit patterns, fp8 tensors uint8 codes.  ``experts=False`` skips the routed
-    expert weights (router-only work).
+    (fp32, or None) when the routed weights are fp8, or w_up_bscale [E,I,d/32]
+    and w_down_bscale [E,d,I/32] (E8M0, or None) when they are fp4, whose
+    codes are then packed two per byte (w_up [E,I,d/2], w_down [E,d,I/2]).
+    bf16 tensors are uint16 bit patterns, fp8 / fp4 tensors uint8 codes.
+    ``experts=False`` skips the routed expert weights (router-only work).
     """
     T, d, E, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.inter, wl.shared_inter
     root = np.random.SeedSequence(wl.seed)
@@ -162,6 +201,7 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     out["ws_up"] = _store(_draw(c_sup, (Is, d), 0.02), wl.act_dtype)
     out["ws_down"] = _store(_draw(c_sdown, (d, Is), 0.02), wl.act_dtype)
     out["w_up_scale"] = out["w_down_scale"] = None
+    out["w_up_bscale"] = out["w_down_bscale"] = None
     if not experts:
         return out
 
@@ -172,6 +212,11 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
         w_down = np.empty((E, d, I), np.uint8)
         s_up = np.empty((E, I), np.float32)
         s_down = np.empty((E, d), np.float32)
+    elif wl.expert_dtype == FP4:
+        w_up = np.empty((E, I, d // 2), np.uint8)
+        w_down = np.empty((E, d, I // 2), np.uint8)
+        s_up = np.empty((E, I, d // 32), np.uint8)
+        s_down = np.empty((E, d, I // 32), np.uint8)
     else:
         edt = np.float32 if wl.expert_dtype == F32 else np.uint16
         w_up = np.empty((E, I, d), edt)
@@ -183,6 +228,9 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
         if wl.expert_dtype == FP8:
             w_up[e], s_up[e] = quantize_weight_rows_e4m3(u)
             w_down[e], s_down[e] = quantize_weight_rows_e4m3(dn)
+        elif wl.expert_dtype == FP4:
+            w_up[e], s_up[e] = quantize_weight_rows_mxfp4(u)
+            w_down[e], s_down[e] = quantize_weight_rows_mxfp4(dn)
         else:
             w_up[e] = _store(u, wl.expert_dtype)
             w_down[e] = _store(dn, wl.expert_dtype)
@@ -192,4 +240,6 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     out["w_up"], out["w_down"] = w_up, w_down
     if wl.expert_dtype == FP8:
         out["w_up_scale"], out["w_down_scale"] = s_up, s_down
+    elif wl.expert_dtype == FP4:
+        out["w_up_bscale"], out["w_down_bscale"] = s_up, s_down
     return out

@@ -27,9 +27,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP4 = 0, 1, 2, 3
 EXACT, AS_CONFIGURED = 0, 1
-_DT = {"f32": F32, "bf16": BF16, "fp8": FP8}
+_DT = {"f32": F32, "bf16": BF16, "fp8": FP8, "fp4": FP4}
 
 
 class _Cfg(ctypes.Structure):
@@ -102,6 +102,22 @@ def e4m3_decode(c) -> np.ndarray:
     return out
 
 
+def e2m1_decode(c) -> np.ndarray:
+    """OCP e2m1 codes (low 4 bits of each byte) -> fp64."""
+    c = _c(np.asarray(c, dtype=np.uint8))
+    out = np.empty(c.shape, np.float64)
+    lib().orc_e2m1_to_double_array(_p(c), _p(out), ctypes.c_int64(c.size))
+    return out
+
+
+def e8m0_decode(x) -> np.ndarray:
+    """OCP MX E8M0 scales -> fp64 powers of two."""
+    x = _c(np.asarray(x, dtype=np.uint8))
+    out = np.empty(x.shape, np.float64)
+    lib().orc_e8m0_to_double_array(_p(x), _p(out), ctypes.c_int64(x.size))
+    return out
+
+
 def quantize_rows(v):
     """Per-row e4m3 quantiser in fp32 arithmetic: (codes, fp32 scales)."""
     v = _c(np.asarray(v, dtype=np.float32))
@@ -153,8 +169,9 @@ def forward(wl, inp: dict, tokens=None, mode: int = AS_CONFIGURED):
     m = np.empty(n, np.float64)
     cfg = _cfg(wl)
     args = [_c(inp["w_gate"]), _c(inp["e_bias"], np.float32), _c(inp["w_up"]),
-            _c(inp.get("w_up_scale")), _c(inp["w_down"]), _c(inp.get("w_down_scale")),
-            _c(inp["ws_up"]), _c(inp["ws_down"])]
+            _c(inp.get("w_up_scale")), _c(inp.get("w_up_bscale")), _c(inp["w_down"]),
+            _c(inp.get("w_down_scale")), _c(inp.get("w_down_bscale")), _c(inp["ws_up"]),
+            _c(inp["ws_down"])]
     rc = lib().orc_forward(ctypes.byref(cfg), ctypes.c_int64(n), _p(tokens), _p(x),
                            *[_p(a) for a in args], ctypes.c_int(mode), _p(y), _p(idx), _p(w),
                            _p(m))
@@ -164,18 +181,25 @@ def forward(wl, inp: dict, tokens=None, mode: int = AS_CONFIGURED):
 
 
 def ffn_rows(a, a_dtype: str, rows, mats, w_up, w_down, w_dtype: str, w_up_scale=None,
-             w_down_scale=None, quant_a: bool = False, mode: int = AS_CONFIGURED):
-    """out[p] = Wdown[mats[p]] relu(Wup[mats[p]] a[rows[p]])^2, fp64 [n, d]."""
+             w_down_scale=None, quant_a: bool = False, mode: int = AS_CONFIGURED,
+             w_up_bscale=None, w_down_bscale=None):
+    """out[p] = Wdown[mats[p]] relu(Wup[mats[p]] a[rows[p]])^2, fp64 [n, d].
+
+    fp8 weights take per-row scales; fp4 weights (two codes per byte) take
+    E8M0 block scales, one per 32 elements (``*_bscale``)."""
     a = _c(a)
     w_up, w_down = _c(w_up), _c(w_down)
     inter, d = w_up.shape[-2], w_up.shape[-1]
+    if w_dtype == "fp4":
+        d *= 2
     rows = _c(np.asarray(rows, np.int32))
     mats = _c(np.asarray(mats, np.int32))
     out = np.empty((rows.size, d), np.float64)
     lib().orc_ffn_rows(ctypes.c_int64(d), ctypes.c_int64(inter), _p(a), ctypes.c_int(_DT[a_dtype]),
                        ctypes.c_int64(rows.size), _p(rows), _p(mats), _p(w_up),
-                       _p(_c(w_up_scale, np.float32)), _p(w_down),
-                       _p(_c(w_down_scale, np.float32)), ctypes.c_int(_DT[w_dtype]),
+                       _p(_c(w_up_scale, np.float32)), _p(_c(w_up_bscale, np.uint8)), _p(w_down),
+                       _p(_c(w_down_scale, np.float32)), _p(_c(w_down_bscale, np.uint8)),
+                       ctypes.c_int(_DT[w_dtype]),
                        ctypes.c_int(int(quant_a)), ctypes.c_int(mode), _p(out))
     return out
 

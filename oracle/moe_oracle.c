@@ -47,6 +47,13 @@
  *                      routed GEMMs.  The shared expert and the router keep
  *                      x as stored.
  *
+ * 4-bit experts (vllm.cpp PR "spec(MODEL-TEXT-nemotron-h)": the published
+ * checkpoint keeps its experts in a 4-bit W4A16 format; here the OCP MX
+ * format MXFP4 stands in for it): a weight is an OCP e2m1 code (1 sign,
+ * 2 exponent, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6) times the E8M0
+ * scale 2^(X - 127) of its block of 32 along the input dimension.
+ * Activations stay bf16 (W4A16): x is used as stored and h is held in bf16.
+ *
  * fp8 e4m3 per-row quantiser (OCP 8-bit floating point spec, E4M3 encoding:
  * bias 7, 3 mantissa bits, max 448, no infinities, S.1111.111 is NaN), all in
  * fp32 arithmetic: amax = max|v_i|; s = amax / 448 (0 -> 1); q_i = nearest
@@ -60,6 +67,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_FP8 2
+#define ORC_FP4 3
 
 #define ORC_EXACT 0
 #define ORC_AS_CONFIGURED 1
@@ -82,7 +90,7 @@ typedef struct {
 #include <omp.h>
 #endif
 
-int orc_version(void) { return 3; }
+int orc_version(void) { return 4; }
 
 /* Threads an OpenMP loop of the oracle uses. */
 int orc_num_threads(void) {
@@ -128,6 +136,20 @@ double orc_e4m3_to_double(uint8_t c) {
   if (E == 15 && M == 7) return NAN;
   double mag = (E == 0) ? ldexp((double)M, -9) : ldexp(1.0 + M / 8.0, E - 7);
   return s ? -mag : mag;
+}
+
+/* OCP e2m1 (4 bits: sign, 2 exponent bits with bias 1, 1 mantissa bit) */
+double orc_e2m1_to_double(uint8_t c) {
+  int s = (c >> 3) & 1, E = (c >> 1) & 3, M = c & 1;
+  double mag = (E == 0) ? 0.5 * M : ldexp(1.0 + 0.5 * M, E - 1);
+  return s ? -mag : mag;
+}
+void orc_e2m1_to_double_array(const uint8_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_to_double(in[i]);
+}
+double orc_e8m0_to_double(uint8_t x);
+void orc_e8m0_to_double_array(const uint8_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e8m0_to_double(in[i]);
 }
 
 uint8_t orc_e4m3_from_float(float vf) {
@@ -184,44 +206,79 @@ void orc_quantize_rows(const float* v, int64_t rows, int64_t cols, uint8_t* q, f
 
 /* --------------------------------------------------------- stored values */
 
-/* Widen row `row` (length n) of a stored matrix to fp64.  fp8 rows are
- * multiplied by their row scale. */
-static void widen_row(const void* base, int dtype, const float* row_scale, int64_t row,
-                      int64_t n, double* out) {
-  if (dtype == ORC_F32) {
-    const float* p = (const float*)base + row * n;
+/* OCP MX E8M0 scale: 2^(X - 127) (X = 255 is NaN) */
+double orc_e8m0_to_double(uint8_t x) { return x == 255 ? NAN : ldexp(1.0, (int)x - 127); }
+
+/* A stored weight matrix: elements of dtype `dt` at `w`; fp8 rows carry one
+ * fp32 scale each (`row_scale`); fp4 rows hold two codes per byte (element
+ * 2i in the low nibble of byte i) and one E8M0 scale per block of 32
+ * elements (`bscale`, [rows, n / 32]). */
+typedef struct {
+  const void* w;
+  int dt;
+  const float* row_scale;
+  const uint8_t* bscale;
+} orc_mat;
+
+static orc_mat plain_mat(const void* w, int dt) {
+  orc_mat m = {w, dt, NULL, NULL};
+  return m;
+}
+
+/* Widen row `row` (length n) of a stored matrix to fp64 (scales applied). */
+static void widen_row(orc_mat m, int64_t row, int64_t n, double* out) {
+  if (m.dt == ORC_F32) {
+    const float* p = (const float*)m.w + row * n;
     for (int64_t i = 0; i < n; ++i) out[i] = (double)p[i];
-  } else if (dtype == ORC_BF16) {
-    const uint16_t* p = (const uint16_t*)base + row * n;
+  } else if (m.dt == ORC_BF16) {
+    const uint16_t* p = (const uint16_t*)m.w + row * n;
     for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_to_double(p[i]);
-  } else {
-    const uint8_t* p = (const uint8_t*)base + row * n;
-    double s = (double)row_scale[row];
+  } else if (m.dt == ORC_FP8) {
+    const uint8_t* p = (const uint8_t*)m.w + row * n;
+    double s = (double)m.row_scale[row];
     for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_to_double(p[i]) * s;
+  } else {
+    const uint8_t* p = (const uint8_t*)m.w + row * (n / 2);
+    const uint8_t* bs = m.bscale + row * (n / 32);
+    for (int64_t i = 0; i < n; ++i) {
+      uint8_t c = (i & 1) ? (p[i / 2] >> 4) : (p[i / 2] & 15);
+      out[i] = orc_e2m1_to_double(c) * orc_e8m0_to_double(bs[i / 32]);
+    }
   }
 }
 
 /* dot of an fp64 vector with row `row` of a stored matrix */
-static double dot_row(const double* a, const void* base, int dtype, const float* row_scale,
-                      int64_t row, int64_t n) {
+static double dot_row(const double* a, orc_mat m, int64_t row, int64_t n) {
   double acc = 0.0;
-  if (dtype == ORC_F32) {
-    const float* p = (const float*)base + row * n;
+  if (m.dt == ORC_F32) {
+    const float* p = (const float*)m.w + row * n;
     for (int64_t i = 0; i < n; ++i) acc += a[i] * (double)p[i];
-  } else if (dtype == ORC_BF16) {
-    const uint16_t* p = (const uint16_t*)base + row * n;
+  } else if (m.dt == ORC_BF16) {
+    const uint16_t* p = (const uint16_t*)m.w + row * n;
     for (int64_t i = 0; i < n; ++i) {
       uint32_t u = (uint32_t)p[i] << 16;
       float f;
       memcpy(&f, &u, 4);
       acc += a[i] * (double)f;
     }
-  } else {
-    const uint8_t* p = (const uint8_t*)base + row * n;
-    double s = (double)row_scale[row];
+  } else if (m.dt == ORC_FP8) {
+    const uint8_t* p = (const uint8_t*)m.w + row * n;
+    double s = (double)m.row_scale[row];
     double part = 0.0;
     for (int64_t i = 0; i < n; ++i) part += a[i] * orc_e4m3_to_double(p[i]);
     acc = part * s; /* the row scale is a common factor of the row */
+  } else {
+    /* each block of 32 shares its E8M0 scale */
+    const uint8_t* p = (const uint8_t*)m.w + row * (n / 2);
+    const uint8_t* bs = m.bscale + row * (n / 32);
+    for (int64_t b = 0; b < n / 32; ++b) {
+      double part = 0.0;
+      for (int64_t i = b * 32; i < b * 32 + 32; ++i) {
+        uint8_t c = (i & 1) ? (p[i / 2] >> 4) : (p[i / 2] & 15);
+        part += a[i] * orc_e2m1_to_double(c);
+      }
+      acc += part * orc_e8m0_to_double(bs[b]);
+    }
   }
   return acc;
 }
@@ -315,8 +372,8 @@ int orc_route(const orc_cfg* cfg, int64_t T, const void* x, const void* w_gate,
     char* flags = (char*)malloc(G + E);
 #pragma omp for schedule(dynamic, 16)
     for (int64_t t = 0; t < T; ++t) {
-      widen_row(x, cfg->act_dtype, NULL, t, d, xa);
-      for (int e = 0; e < E; ++e) l[e] = dot_row(xa, w_gate, cfg->act_dtype, NULL, e, d);
+      widen_row(plain_mat(x, cfg->act_dtype), t, d, xa);
+      for (int e = 0; e < E; ++e) l[e] = dot_row(xa, plain_mat(w_gate, cfg->act_dtype), e, d);
       if (logits_out)
         for (int e = 0; e < E; ++e) logits_out[t * E + e] = l[e];
       select_token(cfg, l, e_bias, topk_idx + t * cfg->top_k, topk_w + t * cfg->top_k,
@@ -332,10 +389,10 @@ int orc_route(const orc_cfg* cfg, int64_t T, const void* x, const void* w_gate,
 /* -------------------------------------------------------------- one FFN */
 
 /* h = relu(u)^2 held as the GEMM that reads it holds it (see modes above).
- * `hq`, `hs` are fp32 scratch of length `inter`. */
+ * `hf` is fp32 scratch of length 2 * inter. */
 static void hold_h(double* h, int64_t inter, int w_dtype, int mode, float* hf) {
   if (mode == ORC_EXACT) return;
-  if (w_dtype == ORC_BF16) {
+  if (w_dtype == ORC_BF16 || w_dtype == ORC_FP4) {
     for (int64_t n = 0; n < inter; ++n) h[n] = orc_bf16_to_double(orc_bf16_from_double(h[n]));
   } else if (w_dtype == ORC_F32) {
     for (int64_t n = 0; n < inter; ++n) h[n] = (double)(float)h[n];
@@ -349,19 +406,33 @@ static void hold_h(double* h, int64_t inter, int w_dtype, int mode, float* hf) {
 }
 
 /* out[c] = sum_n Wdown[c,n] * hold(relu(sum_i a_i Wup[n,i])^2), c < d */
-static void ffn_one(const double* a, int64_t d, int64_t inter, const void* w_up,
-                    const float* up_scale, const void* w_down, const float* down_scale,
-                    int w_dtype, int mode, double* h, float* hf, double* out) {
+static void ffn_one(const double* a, int64_t d, int64_t inter, orc_mat up, orc_mat down,
+                    int mode, double* h, float* hf, double* out) {
   for (int64_t n = 0; n < inter; ++n) {
-    double u = dot_row(a, w_up, w_dtype, up_scale, n, d);
+    double u = dot_row(a, up, n, d);
     double r = u > 0.0 ? u : 0.0;
     h[n] = r * r;
   }
-  hold_h(h, inter, w_dtype, mode, hf);
-  for (int64_t c = 0; c < d; ++c) out[c] = dot_row(h, w_down, w_dtype, down_scale, c, inter);
+  hold_h(h, inter, up.dt, mode, hf);
+  for (int64_t c = 0; c < d; ++c) out[c] = dot_row(h, down, c, inter);
 }
 
-static size_t w_elem_size(int dt) { return dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : 1; }
+/* Matrix e of a stack of [rows, cols] matrices of dtype dt.  fp8: `scale`
+ * holds one fp32 scale per row ([n_mats, rows]).  fp4: `bscale` holds the
+ * E8M0 block scales ([n_mats, rows, cols / 32]). */
+static orc_mat stack_mat(const void* w, int dt, const float* scale, const uint8_t* bscale,
+                         int64_t e, int64_t rows, int64_t cols) {
+  orc_mat m = plain_mat(w, dt);
+  if (dt == ORC_FP4) {
+    m.w = (const char*)w + (size_t)e * rows * (cols / 2);
+    m.bscale = bscale + (size_t)e * rows * (cols / 32);
+  } else {
+    size_t esz = dt == ORC_F32 ? 4 : dt == ORC_BF16 ? 2 : 1;
+    m.w = (const char*)w + (size_t)e * rows * cols * esz;
+    if (dt == ORC_FP8) m.row_scale = scale + e * rows;
+  }
+  return m;
+}
 
 /* The activation row the routed GEMMs read: x as stored, or (fp8 routed
  * weights, as-configured mode) x quantised per token. */
@@ -378,17 +449,18 @@ static void routed_input(const orc_cfg* cfg, const void* x, int64_t t, int mode,
     memcpy(xr, xa, sizeof(double) * d);
   }
   (void)x;
+  (void)t;
 }
 
 /* FFN outputs for explicit (row, matrix) pairs: out[p] = FFN_{mat[p]}(a[row[p]]).
  * `a` is [a_rows, d] of dtype a_dtype; matrices are stacked [n_mats, inter, d]
- * and [n_mats, d, inter] of dtype w_dtype (fp8: scales [n_mats, inter] and
- * [n_mats, d]).  quant_a quantises each a row per row before the GEMMs. */
+ * and [n_mats, d, inter] of dtype w_dtype with their scales as stack_mat
+ * reads them.  quant_a quantises each a row to e4m3 before the GEMMs. */
 int orc_ffn_rows(int64_t d, int64_t inter, const void* a, int a_dtype, int64_t n_pairs,
                  const int32_t* row, const int32_t* mat, const void* w_up,
-                 const float* w_up_scale, const void* w_down, const float* w_down_scale,
-                 int w_dtype, int quant_a, int mode, double* out) {
-  size_t esz = w_elem_size(w_dtype);
+                 const float* w_up_scale, const uint8_t* w_up_bscale, const void* w_down,
+                 const float* w_down_scale, const uint8_t* w_down_bscale, int w_dtype,
+                 int quant_a, int mode, double* out) {
 #pragma omp parallel
   {
     double* xa = (double*)malloc(sizeof(double) * d);
@@ -398,7 +470,7 @@ int orc_ffn_rows(int64_t d, int64_t inter, const void* a, int a_dtype, int64_t n
 #pragma omp for schedule(dynamic, 1)
     for (int64_t p = 0; p < n_pairs; ++p) {
       int64_t e = mat[p];
-      widen_row(a, a_dtype, NULL, row[p], d, xa);
+      widen_row(plain_mat(a, a_dtype), row[p], d, xa);
       if (quant_a) {
         uint8_t* q = (uint8_t*)(hf + d);
         float s;
@@ -408,10 +480,8 @@ int orc_ffn_rows(int64_t d, int64_t inter, const void* a, int a_dtype, int64_t n
       } else {
         memcpy(xr, xa, sizeof(double) * d);
       }
-      const char* up = (const char*)w_up + (size_t)e * inter * d * esz;
-      const char* dn = (const char*)w_down + (size_t)e * d * inter * esz;
-      ffn_one(xr, d, inter, up, w_up_scale ? w_up_scale + e * inter : NULL, dn,
-              w_down_scale ? w_down_scale + e * d : NULL, w_dtype, mode, h, hf,
+      ffn_one(xr, d, inter, stack_mat(w_up, w_dtype, w_up_scale, w_up_bscale, e, inter, d),
+              stack_mat(w_down, w_dtype, w_down_scale, w_down_bscale, e, d, inter), mode, h, hf,
               out + p * d);
     }
     free(xa);
@@ -428,15 +498,15 @@ int orc_ffn_rows(int64_t d, int64_t inter, const void* a, int a_dtype, int64_t n
  * plus their routing (topk_idx [n_tok,k], topk_w [n_tok,k], margin [n_tok]). */
 int orc_forward(const orc_cfg* cfg, int64_t n_tok, const int64_t* tokens, const void* x,
                 const void* w_gate, const float* e_bias, const void* w_up,
-                const float* w_up_scale, const void* w_down, const float* w_down_scale,
-                const void* ws_up, const void* ws_down, int mode, double* y,
-                int32_t* topk_idx, double* topk_w, double* margin) {
+                const float* w_up_scale, const uint8_t* w_up_bscale, const void* w_down,
+                const float* w_down_scale, const uint8_t* w_down_bscale, const void* ws_up,
+                const void* ws_down, int mode, double* y, int32_t* topk_idx, double* topk_w,
+                double* margin) {
   const int E = cfg->n_experts, G = cfg->n_group, k = cfg->top_k;
   const int64_t d = cfg->hidden, I = cfg->inter, Is = cfg->shared_inter;
   if (G <= 0 || E % G || cfg->topk_group < 1 || cfg->topk_group > G || k < 1 ||
       k > cfg->topk_group * (E / G))
     return -1;
-  size_t esz = w_elem_size(cfg->expert_dtype);
   int64_t hmax = I > Is ? I : Is;
 #pragma omp parallel
   {
@@ -453,22 +523,22 @@ int orc_forward(const orc_cfg* cfg, int64_t n_tok, const int64_t* tokens, const 
       double* yt = y + p * d;
       int32_t* it = topk_idx + p * k;
       double* wt = topk_w + p * k;
-      widen_row(x, cfg->act_dtype, NULL, t, d, xa);
-      for (int e = 0; e < E; ++e) l[e] = dot_row(xa, w_gate, cfg->act_dtype, NULL, e, d);
+      widen_row(plain_mat(x, cfg->act_dtype), t, d, xa);
+      for (int e = 0; e < E; ++e) l[e] = dot_row(xa, plain_mat(w_gate, cfg->act_dtype), e, d);
       select_token(cfg, l, e_bias, it, wt, margin + p, l + E, l + 2 * E, l + 3 * E, flags,
                    flags + G);
       routed_input(cfg, x, t, mode, xa, xr, hf);
       for (int64_t c = 0; c < d; ++c) yt[c] = 0.0;
       for (int j = 0; j < k; ++j) {
         int64_t e = it[j];
-        const char* up = (const char*)w_up + (size_t)e * I * d * esz;
-        const char* dn = (const char*)w_down + (size_t)e * d * I * esz;
-        ffn_one(xr, d, I, up, w_up_scale ? w_up_scale + e * I : NULL, dn,
-                w_down_scale ? w_down_scale + e * d : NULL, cfg->expert_dtype, mode, h, hf, o);
+        const int dt = cfg->expert_dtype;
+        ffn_one(xr, d, I, stack_mat(w_up, dt, w_up_scale, w_up_bscale, e, I, d),
+                stack_mat(w_down, dt, w_down_scale, w_down_bscale, e, d, I), mode, h, hf, o);
         for (int64_t c = 0; c < d; ++c) yt[c] += wt[j] * o[c];
       }
       if (Is > 0) {
-        ffn_one(xa, d, Is, ws_up, NULL, ws_down, NULL, cfg->act_dtype, mode, h, hf, o);
+        ffn_one(xa, d, Is, plain_mat(ws_up, cfg->act_dtype), plain_mat(ws_down, cfg->act_dtype),
+                mode, h, hf, o);
         for (int64_t c = 0; c < d; ++c) yt[c] += o[c];
       }
     }
