@@ -57,13 +57,18 @@ class Workload:
     top_k: int              # k            (num_experts_per_tok)
     inter: int              # I            (moe_intermediate_size)
     shared_inter: int       # Is           (moe_shared_expert_intermediate_size)
-    act_dtype: str          # x, w_gate, shared weights, y
+    act_dtype: str          # x, w_gate, y, and the shared weights unless shared_dtype
     expert_dtype: str       # routed expert weights
     norm_topk_prob: bool = True
     routed_scaling_factor: float = 2.5
     bias_boost: tuple = ()  # experts whose correction bias is raised
     bias_boost_value: float = 0.0
     seed: int = 0
+    shared_dtype: str = None  # shared-expert weights; None = act_dtype
+
+    @property
+    def shared_weight_dtype(self) -> str:
+        return self.shared_dtype or self.act_dtype
 
     def with_tokens(self, tokens: int) -> "Workload":
         return dataclasses.replace(self, tokens=int(tokens))
@@ -83,9 +88,9 @@ WORKLOADS = {
                                  bias_boost=(0, 4, 8, 12, 64, 68, 72, 76), bias_boost_value=2.0,
                                  **_NEMOTRON),
     "fp8-T8192": Workload("fp8-T8192", 8192, act_dtype=BF16, expert_dtype=FP8, **_NEMOTRON),
-    # routed experts in 4-bit MXFP4 (W4A16: activations and h stay bf16)
+    # routed and shared experts in 4-bit MXFP4 (W4A16: activations and h stay bf16)
     "decode-fp4-T32": Workload("decode-fp4-T32", 32, act_dtype=BF16, expert_dtype=FP4,
-                               **_NEMOTRON),
+                               shared_dtype=FP4, **_NEMOTRON),
 }
 
 
@@ -183,7 +188,9 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     ws_up [Is,d], ws_down [d,Is]; plus w_up_scale [E,I] and w_down_scale [E,d]
     (fp32, or None) when the routed weights are fp8, or w_up_bscale [E,I,d/32]
     and w_down_bscale [E,d,I/32] (E8M0, or None) when they are fp4, whose
-    codes are then packed two per byte (w_up [E,I,d/2], w_down [E,d,I/2]).
+    codes are then packed two per byte (w_up [E,I,d/2], w_down [E,d,I/2]);
+    likewise ws_up_bscale [Is,d/32] and ws_down_bscale [d,Is/32] with packed
+    ws_up [Is,d/2] and ws_down [d,Is/2] when the shared expert is fp4.
     bf16 tensors are uint16 bit patterns, fp8 / fp4 tensors uint8 codes.
     ``experts=False`` skips the routed expert weights (router-only work).
     """
@@ -198,10 +205,16 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     for e in wl.bias_boost:
         b[e] = b[e] + np.float32(wl.bias_boost_value)
     out["e_bias"] = b.astype(np.float32)
-    out["ws_up"] = _store(_draw(c_sup, (Is, d), 0.02), wl.act_dtype)
-    out["ws_down"] = _store(_draw(c_sdown, (d, Is), 0.02), wl.act_dtype)
     out["w_up_scale"] = out["w_down_scale"] = None
     out["w_up_bscale"] = out["w_down_bscale"] = None
+    out["ws_up_bscale"] = out["ws_down_bscale"] = None
+    sup, sdown = _draw(c_sup, (Is, d), 0.02), _draw(c_sdown, (d, Is), 0.02)
+    if wl.shared_weight_dtype == FP4:
+        out["ws_up"], out["ws_up_bscale"] = quantize_weight_rows_mxfp4(sup)
+        out["ws_down"], out["ws_down_bscale"] = quantize_weight_rows_mxfp4(sdown)
+    else:
+        out["ws_up"] = _store(sup, wl.shared_weight_dtype)
+        out["ws_down"] = _store(sdown, wl.shared_weight_dtype)
     if not experts:
         return out
 

@@ -38,7 +38,7 @@ class _Cfg(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_double), ("act_dtype", ctypes.c_int32),
-                ("expert_dtype", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("shared_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -68,7 +68,8 @@ def _p(a):
 def _cfg(wl):
     return _Cfg(wl.hidden, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k, wl.inter,
                 wl.shared_inter, int(bool(wl.norm_topk_prob)), float(wl.routed_scaling_factor),
-                _DT[wl.act_dtype], _DT[wl.expert_dtype])
+                _DT[wl.act_dtype], _DT[wl.expert_dtype],
+                _DT[getattr(wl, "shared_dtype", None) or wl.act_dtype])
 
 
 def _c(a, dtype=None):
@@ -171,7 +172,7 @@ def forward(wl, inp: dict, tokens=None, mode: int = AS_CONFIGURED):
     args = [_c(inp["w_gate"]), _c(inp["e_bias"], np.float32), _c(inp["w_up"]),
             _c(inp.get("w_up_scale")), _c(inp.get("w_up_bscale")), _c(inp["w_down"]),
             _c(inp.get("w_down_scale")), _c(inp.get("w_down_bscale")), _c(inp["ws_up"]),
-            _c(inp["ws_down"])]
+            _c(inp.get("ws_up_bscale")), _c(inp["ws_down"]), _c(inp.get("ws_down_bscale"))]
     rc = lib().orc_forward(ctypes.byref(cfg), ctypes.c_int64(n), _p(tokens), _p(x),
                            *[_p(a) for a in args], ctypes.c_int(mode), _p(y), _p(idx), _p(w),
                            _p(m))

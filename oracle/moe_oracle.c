@@ -53,6 +53,8 @@
  * 2 exponent, 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6) times the E8M0
  * scale 2^(X - 127) of its block of 32 along the input dimension.
  * Activations stay bf16 (W4A16): x is used as stored and h is held in bf16.
+ * The same checkpoint holds its shared experts in that 4-bit format too, so
+ * the shared expert may take fp4 weights (shared_dtype) like the routed ones.
  *
  * fp8 e4m3 per-row quantiser (OCP 8-bit floating point spec, E4M3 encoding:
  * bias 7, 3 mantissa bits, max 448, no infinities, S.1111.111 is NaN), all in
@@ -82,15 +84,16 @@ typedef struct {
   int32_t shared_inter; /* Is, 0 = no shared expert */
   int32_t norm_topk_prob;
   double routed_scaling_factor;
-  int32_t act_dtype;    /* x, w_gate, shared weights */
+  int32_t act_dtype;    /* x, w_gate, y */
   int32_t expert_dtype; /* routed weights */
+  int32_t shared_dtype; /* shared-expert weights: act_dtype, or ORC_FP4 */
 } orc_cfg;
 
 #ifdef _OPENMP
 #include <omp.h>
 #endif
 
-int orc_version(void) { return 4; }
+int orc_version(void) { return 5; }
 
 /* Threads an OpenMP loop of the oracle uses. */
 int orc_num_threads(void) {
@@ -500,8 +503,8 @@ int orc_forward(const orc_cfg* cfg, int64_t n_tok, const int64_t* tokens, const 
                 const void* w_gate, const float* e_bias, const void* w_up,
                 const float* w_up_scale, const uint8_t* w_up_bscale, const void* w_down,
                 const float* w_down_scale, const uint8_t* w_down_bscale, const void* ws_up,
-                const void* ws_down, int mode, double* y, int32_t* topk_idx, double* topk_w,
-                double* margin) {
+                const uint8_t* ws_up_bscale, const void* ws_down, const uint8_t* ws_down_bscale,
+                int mode, double* y, int32_t* topk_idx, double* topk_w, double* margin) {
   const int E = cfg->n_experts, G = cfg->n_group, k = cfg->top_k;
   const int64_t d = cfg->hidden, I = cfg->inter, Is = cfg->shared_inter;
   if (G <= 0 || E % G || cfg->topk_group < 1 || cfg->topk_group > G || k < 1 ||
@@ -537,8 +540,9 @@ int orc_forward(const orc_cfg* cfg, int64_t n_tok, const int64_t* tokens, const 
         for (int64_t c = 0; c < d; ++c) yt[c] += wt[j] * o[c];
       }
       if (Is > 0) {
-        ffn_one(xa, d, Is, plain_mat(ws_up, cfg->act_dtype), plain_mat(ws_down, cfg->act_dtype),
-                mode, h, hf, o);
+        const int sdt = cfg->shared_dtype;
+        ffn_one(xa, d, Is, stack_mat(ws_up, sdt, NULL, ws_up_bscale, 0, Is, d),
+                stack_mat(ws_down, sdt, NULL, ws_down_bscale, 0, d, Is), mode, h, hf, o);
         for (int64_t c = 0; c < d; ++c) yt[c] += o[c];
       }
     }

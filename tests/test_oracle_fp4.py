@@ -6,6 +6,7 @@ bf16 value, so the two are the same mathematics on the same numbers)."""
 import dataclasses
 
 import numpy as np
+import pytest
 
 import oracle
 from non_gated_relu_amd import synthetic
@@ -111,17 +112,25 @@ def test_fp4_ffn_brute_force_one_row():
     np.testing.assert_allclose(got[0], ref, rtol=1e-5, atol=1e-6 * np.abs(ref).max())
 
 
-def test_fp4_forward_equals_bf16_forward_on_the_dequantised_weights():
+@pytest.mark.parametrize("shared", ["bf16", "fp4"])
+def test_fp4_forward_equals_bf16_forward_on_the_dequantised_weights(shared):
     wl = synthetic.Workload("fp4-tiny", 40, hidden=64, n_experts=16, n_group=4,
                             topk_group=1, top_k=2, inter=96, shared_inter=64,
-                            act_dtype="bf16", expert_dtype="fp4", seed=11)
+                            act_dtype="bf16", expert_dtype="fp4", seed=11, shared_dtype=shared)
     inp = synthetic.make_inputs(wl)
     got = oracle.forward(wl, inp)
     ref_inp = dict(inp)
-    ref_inp["w_up"] = f32_to_bf16_bits(_dequant(inp["w_up"], inp["w_up_bscale"]).astype(np.float32))
-    ref_inp["w_down"] = f32_to_bf16_bits(
-        _dequant(inp["w_down"], inp["w_down_bscale"]).astype(np.float32))
-    ref_inp["w_up_bscale"] = ref_inp["w_down_bscale"] = None
-    ref = oracle.forward(dataclasses.replace(wl, expert_dtype="bf16"), ref_inp)
+    names = [("w_up", "w_up_bscale"), ("w_down", "w_down_bscale")]
+    if shared == "fp4":
+        names += [("ws_up", "ws_up_bscale"), ("ws_down", "ws_down_bscale")]
+    for w, b in names:
+        ref_inp[w] = f32_to_bf16_bits(_dequant(inp[w], inp[b]).astype(np.float32))
+        ref_inp[b] = None
+    ref = oracle.forward(dataclasses.replace(wl, expert_dtype="bf16", shared_dtype=None), ref_inp)
     np.testing.assert_array_equal(got["topk_idx"], ref["topk_idx"])
     np.testing.assert_array_equal(got["y"], ref["y"])
+    # the shared expert matters: dropping it changes y
+    if shared == "fp4":
+        ref_inp["ws_down"] = np.zeros_like(ref_inp["ws_down"])
+        assert not np.array_equal(oracle.forward(dataclasses.replace(
+            wl, expert_dtype="bf16", shared_dtype=None), ref_inp)["y"], got["y"])
