@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "decode-bf16-T32"
 DEFAULT_STEPS = {"tiny-f32-T64": 200, "decode-bf16-T32": 200, "prefill-bf16-T4096": 50,
-                 "skew-bf16-T16384": 20, "fp8-T8192": 30}
+                 "skew-bf16-T16384": 20, "fp8-T8192": 30, "decode-fp4-T32": 200}
 # kernels whose counter readings are reported as "traffic"
 TRAFFIC_SOURCES = ["non_gated_relu_amd/csrc/gemm.hip", "non_gated_relu_amd/csrc/common.hpp",
                    "non_gated_relu_amd/csrc/internal.hpp"]
@@ -40,44 +40,60 @@ def esize(dt):
     return {"f32": 4, "bf16": 2, "fp8": 1}[dt]
 
 
+def wbytes(dt, rows: int, cols: int) -> int:
+    """Stored bytes of one [rows, cols] weight matrix: its elements, plus the
+    fp32 row scales (fp8) or the E8M0 scale of every 32 elements (fp4)."""
+    if dt == "fp4":
+        return rows * cols // 2 + rows * cols // 32
+    return rows * cols * esize(dt) + (rows * 4 if dt == "fp8" else 0)
+
+
+def mfma_dtype(dt):
+    """Operand type of the MFMA a weight type runs on (fp4 is widened to bf16)."""
+    return "bf16" if dt == "fp4" else dt
+
+
 def stage_work(wl, active: int):
     """Algorithmic bytes and flops of each stage's launch(es) for one step.
 
     Bytes count what the method must move: the weights of the active experts
-    (one unit = one expert projection of I*d elements, plus its fp32 row
-    scales when fp8), the stage's input activations and its outputs.
+    (one unit = one expert projection of I*d elements with its scales: fp32
+    per row for fp8, E8M0 per 32 elements for fp4), the stage's input
+    activations and its outputs.
     """
     T, d, E, k, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
     S = T * k
-    we, ae = esize(wl.expert_dtype), esize(wl.act_dtype)
-    fp8 = wl.expert_dtype == "fp8"
+    ae = esize(wl.act_dtype)
+    edt, sdt = wl.expert_dtype, wl.shared_weight_dtype
+    fp8 = edt == "fp8"
     a_in = 1 if fp8 else ae              # the routed GEMMs read x (fp8: its e4m3 codes)
-    h_out = 4 if fp8 else (4 if wl.expert_dtype == "f32" else 2)  # h as written by the up GEMM
+    h_out = 4 if fp8 or edt == "f32" else 2  # h as written by the up GEMM (bf16 for bf16, fp4)
     h_in = 1 if fp8 else h_out
-    scale_up = active * I * 4 if fp8 else 0
-    scale_dn = active * d * 4 if fp8 else 0
+    up_u, dn_u = wbytes(edt, I, d), wbytes(edt, d, I)
     w = {
         "route": dict(bytes=T * d * ae + E * d * ae + E * 4 + S * 8, flops=2 * T * d * E,
                       dtype=wl.act_dtype),
-        "routed_up": dict(bytes=active * I * d * we + scale_up + T * d * a_in + S * I * h_out,
-                          flops=2 * S * d * I, dtype=wl.expert_dtype, unit_bytes=I * d * we,
+        "routed_up": dict(bytes=active * up_u + T * d * a_in + S * I * h_out,
+                          flops=2 * S * d * I, dtype=mfma_dtype(edt), unit_bytes=up_u,
                           units=active),
-        "routed_down": dict(bytes=active * d * I * we + scale_dn + S * I * h_in + S * d * 4,
-                            flops=2 * S * I * d, dtype=wl.expert_dtype, unit_bytes=d * I * we,
+        "routed_down": dict(bytes=active * dn_u + S * I * h_in + S * d * 4,
+                            flops=2 * S * I * d, dtype=mfma_dtype(edt), unit_bytes=dn_u,
                             units=active),
     }
     if Is:
-        sh_up = dict(bytes=Is * d * ae + T * d * ae + T * Is * ae, flops=2 * T * d * Is)
-        sh_dn = dict(bytes=d * Is * ae + T * Is * ae + T * d * 4, flops=2 * T * Is * d)
-        if wl.expert_dtype == wl.act_dtype:
+        sh_h = 4 if sdt == "f32" else 2
+        su, sd = wbytes(sdt, Is, d), wbytes(sdt, d, Is)
+        sh_up = dict(bytes=su + T * d * ae + T * Is * sh_h, flops=2 * T * d * Is)
+        sh_dn = dict(bytes=sd + T * Is * sh_h + T * d * 4, flops=2 * T * Is * d)
+        if edt == sdt:
             # the shared expert runs inside the routed launches as one more group
-            for st, sh in (("routed_up", sh_up), ("routed_down", sh_dn)):
+            for st, sh, wb in (("routed_up", sh_up, su), ("routed_down", sh_dn, sd)):
                 w[st]["bytes"] += sh["bytes"]
                 w[st]["flops"] += sh["flops"]
-                w[st]["shared_weight_bytes"] = Is * d * ae
+                w[st]["shared_weight_bytes"] = wb
         else:
-            w["shared_up"] = dict(sh_up, dtype=wl.act_dtype, unit_bytes=Is * d * ae, units=1)
-            w["shared_down"] = dict(sh_dn, dtype=wl.act_dtype, unit_bytes=d * Is * ae, units=1)
+            w["shared_up"] = dict(sh_up, dtype=mfma_dtype(sdt), unit_bytes=su, units=1)
+            w["shared_down"] = dict(sh_dn, dtype=mfma_dtype(sdt), unit_bytes=sd, units=1)
     w["combine"] = dict(bytes=S * d * 4 + T * d * 4 * (1 if Is else 0) + T * d * ae + S * 8,
                         flops=0, dtype="f32")
     return w
@@ -86,10 +102,11 @@ def stage_work(wl, active: int):
 def layer_work(wl, active: int):
     """Algorithmic flops and bytes of one whole layer step."""
     T, d, E, k, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
-    we, ae = esize(wl.expert_dtype), esize(wl.act_dtype)
+    ae = esize(wl.act_dtype)
+    edt, sdt = wl.expert_dtype, wl.shared_weight_dtype
     flops = T * (2 * d * E + k * 4 * d * I + 4 * d * Is)
-    scales = active * (I + d) * 4 if wl.expert_dtype == "fp8" else 0
-    byts = active * 2 * I * d * we + scales + 2 * Is * d * ae + E * d * ae + E * 4 + 2 * T * d * ae
+    byts = (active * (wbytes(edt, I, d) + wbytes(edt, d, I)) + wbytes(sdt, Is, d) +
+            wbytes(sdt, d, Is) + E * d * ae + E * 4 + 2 * T * d * ae)
     return flops, byts
 
 
@@ -262,7 +279,8 @@ def main():
     line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
             "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "fp8+bf16" if wl.expert_dtype == "fp8" else wl.act_dtype,
+            "dtype": {"fp8": "fp8+bf16", "fp4": "bf16 (fp4 weights)"}.get(wl.expert_dtype,
+                                                                         wl.act_dtype),
             "data": "synthetic (seeded Gaussian inputs and weights)",
             "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,
                        "experts": wl.n_experts, "groups": wl.n_group,

@@ -20,7 +20,9 @@
  *  - Array arguments are DEVICE pointers unless marked (host); arrays are
  *    row-major and contiguous; every array pointer must be 16-byte aligned.
  *    bf16 arrays hold IEEE bfloat16 bit patterns; fp8 arrays hold OCP e4m3fn
- *    codes.
+ *    codes; fp4 arrays hold OCP MXFP4 data: e2m1 codes two per byte (the
+ *    element of lower index in the low nibble) and, per 32 consecutive
+ *    elements of a row, one E8M0 scale byte (the power of two 2^(code-127)).
  *  - The caller owns every buffer, including the workspace.  The library never
  *    allocates or frees memory, never synchronises, and keeps no state between
  *    calls; all work is enqueued on `stream` (a hipStream_t, NULL = the null
@@ -58,7 +60,13 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_FP8_E4M3 = 2 /* routed expert weights only, with fp32 per-row scales */
+  MOE_FP8_E4M3 = 2, /* routed expert weights only, with fp32 per-row scales   */
+  MOE_FP4_E2M1 = 3  /* routed expert weights only, MXFP4: E8M0 scale per 32
+                       elements.  4-bit experts with 16-bit activations
+                       (W4A16) are the decode configuration of the Nemotron-H
+                       runtime support in vllm.cpp PR
+                       "spec(MODEL-TEXT-nemotron-h)"; MXFP4 is this library's
+                       choice of 4-bit format                               */
 } moe_dtype;
 
 /* Layer configuration; names follow the model config (exo commit "Add support
@@ -75,9 +83,13 @@ typedef struct moe_config {
                             0 = no shared expert                                     */
   int32_t norm_topk_prob;/* 0 or 1                                                   */
   float routed_scaling_factor;
-  int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, w_gate, shared weights, y        */
-  int32_t expert_dtype;  /* routed weights: MOE_F32 (needs act F32), MOE_BF16 or
-                            MOE_FP8_E4M3 (both need act BF16)                        */
+  int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, w_gate, y                        */
+  int32_t expert_dtype;  /* routed weights: MOE_F32 (needs act F32), MOE_BF16,
+                            MOE_FP8_E4M3 or MOE_FP4_E2M1 (these need act BF16)       */
+  int32_t shared_dtype;  /* shared-expert weights: act_dtype, or MOE_FP4_E2M1 when
+                            expert_dtype is MOE_FP4_E2M1 (the 4-bit checkpoint of
+                            vllm.cpp PR "spec(MODEL-TEXT-nemotron-h)" quantises the
+                            shared experts with the routed ones)                    */
 } moe_config;
 
 /* Bytes of workspace moe_forward needs for `tokens` tokens (host output). The
@@ -129,22 +141,29 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
  *                row_offsets[n_mats] = rows (values are clamped to [0, rows])
  *   row_index    [rows] int32 or NULL; index_div >= 1; sources clamp to a_rows-1
  *   w_up         [n_mats, inter, d], w_down [n_mats, d, inter], of w_dtype
- *   w_up_scale   [n_mats, inter], w_down_scale [n_mats, d]: fp32 per-row scales
- *                for MOE_FP8_E4M3 weights, else NULL
+ *                (fp4: [n_mats, inter, d/2] and [n_mats, d, inter/2] bytes)
+ *   w_up_scale, w_down_scale
+ *                MOE_FP8_E4M3: fp32 per-row scales [n_mats, inter] and [n_mats, d];
+ *                MOE_FP4_E2M1: E8M0 block scales (uint8) [n_mats, inter, d/32]
+ *                and [n_mats, d, inter/32], codes 0..254;
+ *                otherwise NULL (ignored)
  *   out          [rows, d] fp32
  * With fp8 weights each a row is quantised per row to e4m3 (scale amax/448,
  * nearest even, saturating) before the up GEMM and each h row likewise before
  * the down GEMM; both GEMMs run on fp8 MFMA with fp32 accumulation and the
- * scales applied in the epilogue.  Otherwise h is rounded to the weights'
- * type (bf16 nearest even, or fp32) and both GEMMs accumulate in fp32.
+ * scales applied in the epilogue.  fp4 weights are widened to bf16 (exact:
+ * an e2m1 value times a power of two is a bf16 value, for scale codes down to
+ * 2^-126) and multiply bf16 a and h on bf16 MFMA.  Otherwise, and for fp4, h
+ * is rounded to bf16 (nearest even; fp32 for fp32 weights) and both GEMMs
+ * accumulate in fp32.
  * The routed experts of the layer are the call (n_mats = E, a = x,
  * row_offsets = expert_offsets, row_index = sorted_slot, index_div = k); the
  * shared expert is (n_mats = 1, row_offsets = {0, tokens}, row_index = NULL). */
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, int32_t w_dtype,
                           int64_t a_rows, const void* a, int64_t rows,
                           const int32_t* row_offsets, const int32_t* row_index,
-                          int32_t index_div, const void* w_up, const float* w_up_scale,
-                          const void* w_down, const float* w_down_scale, float* out,
+                          int32_t index_div, const void* w_up, const void* w_up_scale,
+                          const void* w_down, const void* w_down_scale, float* out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Weighted combine (exo commit "Add support for Nemotron sharding": the shared
@@ -162,15 +181,17 @@ moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slo
  * When the shared expert's weights have the routed experts' type it runs in
  * the routed GEMM launches as one extra group (same arithmetic per element).
  *   x [tokens, d], w_gate [E, d], e_bias [E] fp32, w_up [E, I, d], w_down [E, d, I]
- *   (expert_dtype; fp8 scales as in moe_expert_ffn), ws_up [Is, d], ws_down [d, Is]
- *   (act_dtype), y [tokens, d] act_dtype out.
+ *   (expert_dtype; packing and scales as in moe_expert_ffn), ws_up [Is, d], ws_down [d, Is]
+ *   (shared_dtype; fp4: ws_up_scale [Is, d/32] and ws_down_scale [d, Is/32] E8M0,
+ *   else NULL), y [tokens, d] act_dtype out.
  *   topk_idx [tokens,k], topk_w [tokens,k], expert_counts [E]: optional outputs
  *   (NULL = not wanted).
  *   workspace: at least moe_workspace_size(cfg, tokens) bytes. */
 moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
-                       const float* e_bias, const void* w_up, const float* w_up_scale,
-                       const void* w_down, const float* w_down_scale, const void* ws_up,
-                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
+                       const float* e_bias, const void* w_up, const void* w_up_scale,
+                       const void* w_down, const void* w_down_scale, const void* ws_up,
+                       const void* ws_up_scale, const void* ws_down, const void* ws_down_scale,
+                       void* y, int32_t* topk_idx, float* topk_w,
                        int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                        void* stream);
 
@@ -195,9 +216,11 @@ enum {
 };
 moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
                              const void* w_gate, const float* e_bias, const void* w_up,
-                             const float* w_up_scale, const void* w_down,
-                             const float* w_down_scale, const void* ws_up, const void* ws_down,
-                             void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                             const void* w_up_scale, const void* w_down,
+                             const void* w_down_scale, const void* ws_up,
+                             const void* ws_up_scale, const void* ws_down,
+                             const void* ws_down_scale, void* y, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* const* stage_events);
 

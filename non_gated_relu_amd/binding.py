@@ -16,9 +16,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
-DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
-TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_FP4_E2M1 = 0, 1, 2, 3
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "fp4": MOE_FP4_E2M1}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+               "fp4": torch.uint8}
 
 
 class MoeConfig(ctypes.Structure):
@@ -27,7 +28,7 @@ class MoeConfig(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
                 ("routed_scaling_factor", ctypes.c_float), ("act_dtype", ctypes.c_int32),
-                ("expert_dtype", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("shared_dtype", ctypes.c_int32)]
 
 
 def config_from(wl) -> MoeConfig:
@@ -35,7 +36,8 @@ def config_from(wl) -> MoeConfig:
     return MoeConfig(wl.hidden, wl.n_experts, wl.n_group, wl.topk_group, wl.top_k, wl.inter,
                      wl.shared_inter, int(bool(wl.norm_topk_prob)),
                      float(wl.routed_scaling_factor), DTYPE_CODE[wl.act_dtype],
-                     DTYPE_CODE[wl.expert_dtype])
+                     DTYPE_CODE[wl.expert_dtype],
+                     DTYPE_CODE[getattr(wl, "shared_dtype", None) or wl.act_dtype])
 
 
 _lib = None
@@ -66,7 +68,7 @@ def lib() -> ctypes.CDLL:
                                      _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_combine.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp]
         L.moe_forward.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                  _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                  _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [_vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
@@ -171,10 +173,15 @@ def permute(cfg: MoeConfig, topk_idx, x=None, with_x_perm: bool = False):
 def expert_ffn(cfg: MoeConfig, w_up, w_down, a, row_offsets, rows: int, row_index=None,
                index_div: int = 1, w_dtype: str = None, w_up_scale=None, w_down_scale=None,
                out=None):
-    """out[r] = Wdown[m] relu(Wup[m] a[src(r)])^2 over the grouped rows (see moe.h)."""
+    """out[r] = Wdown[m] relu(Wup[m] a[src(r)])^2 over the grouped rows (see moe.h).
+
+    uint8 weights are fp8 codes, or packed fp4 codes when their rows hold
+    hidden / 2 bytes; the scales are fp32 per row (fp8) or E8M0 blocks (fp4)."""
     n_mats, inter = w_up.shape[0], w_up.shape[1]
-    w_dtype = w_dtype or {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}[
-        w_up.dtype]
+    if w_dtype is None:
+        w_dtype = {torch.float32: "f32", torch.bfloat16: "bf16", torch.uint8: "fp8"}[w_up.dtype]
+        if w_dtype == "fp8" and 2 * w_up.shape[2] == cfg.hidden:
+            w_dtype = "fp4"
     code = DTYPE_CODE[w_dtype]
     a_rows = a.shape[0]
     out = _empty((rows, cfg.hidden), torch.float32, a) if out is None else out
@@ -202,16 +209,20 @@ STAGES = ("route", "permute", "quant_x", "routed_up", "quant_h", "routed_down", 
 
 def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_up_scale=None,
             w_down_scale=None, ws=None, y=None, topk_idx=None, topk_w=None, expert_counts=None,
-            stage_events=None):
-    """moe_forward; with ``stage_events`` (a StageEvents) moe_forward_timed."""
+            stage_events=None, ws_up_scale=None, ws_down_scale=None):
+    """moe_forward; with ``stage_events`` (a StageEvents) moe_forward_timed.
+
+    Scales: fp8 experts take fp32 per-row ``w_*_scale``; fp4 experts take E8M0
+    block scales there, and an fp4 shared expert takes them in ``ws_*_scale``."""
     T = x.shape[0]
     if y is None:
         y = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
     if ws is None:
         ws = workspace(workspace_size(cfg, T), x)
     args = [ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias), _p(w_up), _p(w_up_scale),
-            _p(w_down), _p(w_down_scale), _p(ws_up), _p(ws_down), _p(y), _p(topk_idx),
-            _p(topk_w), _p(expert_counts), _p(ws), ws.numel(), _stream()]
+            _p(w_down), _p(w_down_scale), _p(ws_up), _p(ws_up_scale), _p(ws_down),
+            _p(ws_down_scale), _p(y), _p(topk_idx), _p(topk_w), _p(expert_counts), _p(ws),
+            ws.numel(), _stream()]
     if stage_events is None:
         _check(lib().moe_forward(*args), "moe_forward")
     else:
@@ -243,7 +254,7 @@ def stages_of(wl):
         st += ["quant_x", "routed_up", "quant_h", "routed_down"]
     else:
         st += ["routed_up", "routed_down"]
-    if wl.shared_inter and wl.expert_dtype != wl.act_dtype:
+    if wl.shared_inter and wl.expert_dtype != (getattr(wl, "shared_dtype", None) or wl.act_dtype):
         st += ["shared_up", "shared_down"]
     return st + ["combine"]
 
@@ -275,10 +286,12 @@ class MoELayer:
             raise ValueError(f"{T} tokens exceed the workspace sized for {self.max_tokens}")
         t = self.t
         return forward(self.cfg, x, t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
-                       t.get("ws_up"), t.get("ws_down"), t.get("w_up_scale"),
-                       t.get("w_down_scale"), ws=self.ws, y=y, topk_idx=self.topk_idx[:T],
-                       topk_w=self.topk_w[:T], expert_counts=self.expert_counts,
-                       stage_events=stage_events)
+                       t.get("ws_up"), t.get("ws_down"),
+                       t.get("w_up_scale", t.get("w_up_bscale")),
+                       t.get("w_down_scale", t.get("w_down_bscale")), ws=self.ws, y=y,
+                       topk_idx=self.topk_idx[:T], topk_w=self.topk_w[:T],
+                       expert_counts=self.expert_counts, stage_events=stage_events,
+                       ws_up_scale=t.get("ws_up_bscale"), ws_down_scale=t.get("ws_down_bscale"))
 
 
 class GraphStep:

@@ -11,7 +11,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2 };
+enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_FP4 = 3 };
 
 constexpr int WAVE = 64;
 

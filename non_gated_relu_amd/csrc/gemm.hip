@@ -113,6 +113,7 @@ __device__ __forceinline__ GemmProblem pick_problem(const GemmArgs& pa, bool sec
   p.row_index = second ? b.row_index : a.row_index;
   p.w = second ? b.w : a.w;
   p.w_scale = second ? b.w_scale : a.w_scale;
+  p.w_bscale = second ? b.w_bscale : a.w_bscale;
   p.offsets = second ? b.offsets : a.offsets;
   p.out = second ? b.out : a.out;
   p.a_rows = second ? b.a_rows : a.a_rows;
@@ -753,6 +754,144 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
     store_block<KIND, EPI>(t, acc[j], t.m0 + lgrp * 4, t.n0 + (wave * FN + j) * 16 + lrow);
 }
 
+// ------------------------------------------------------------ fp4 kernel
+//
+// MXFP4 weights (an e2m1 code times the E8M0 power of two of its 32-element
+// block) with bf16 activations.  In decode each weight byte feeds one MFMA
+// or a few, so the launch is a weight stream: the codes go from global
+// memory straight into registers, 16 bytes (one scale block of one row) per
+// lane, and are widened where the fragment is built by
+// v_cvt_scalef32_pk_bf16_fp4, which applies the block's power of two.  An
+// e2m1 value times a power of two is a bf16 value, so the MFMA sees the
+// dequantised weight exactly.
+//
+// The NW waves of a workgroup split K: wave w takes a contiguous run of
+// 128-element super-blocks.  In super-block b, lane group g (lanes 16 g ..
+// 16 g + 15, one per row) owns scale block 4 b + g, and MFMA step s (0..3)
+// gives every lane elements 8 s .. 8 s + 7 of its own block, of the
+// activation row and of the weight row alike; the four steps cover the 128
+// elements once.  The waves' partial tiles are then summed through LDS in
+// wave order (a fixed order, so results are deterministic) and stored by the
+// usual epilogue.  A rows past the group end are never read.
+constexpr int F4_SB_BLOCKS = 4;  // 32-element scale blocks per super-block
+constexpr int F4_WAVES = 8;
+
+__device__ __forceinline__ i32x4_t fp4x8_to_bf16(uint32_t codes, float scale) {
+  i32x4_t r;
+  r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return r;
+}
+
+// P super-blocks of loads are issued together before their MFMAs.
+template <int BM, int BN, int EPI, int NW, int P>
+__global__ __launch_bounds__(NW * WAVE) void gemm_fp4_kernel(GemmArgs pa) {
+  constexpr int FM = BM / 16, FN = BN / 16;
+  constexpr int UNITS = FM * FN * WAVE;  // f32x4 partial results per wave
+  __shared__ f32x4_t red[NW * UNITS];
+
+  Tile t;
+  if (!locate_tile<BM, BN>(pa, t, blockIdx.x)) return;
+  const GemmProblem& p = t.p;
+  const int wave = threadIdx.x / WAVE;
+  const int lane = lane_id();
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int nblk = p.k / 32;  // scale blocks per row (the host guarantees K % 64 == 0)
+  const int nsb = (nblk + F4_SB_BLOCKS - 1) / F4_SB_BLOCKS;
+  const int sb0 = wave * nsb / NW;
+  const int sb1 = (wave + 1) * nsb / NW;
+
+  const char* arow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t r = t.m0 + 16 * i + lrow;
+    arow[i] = r < t.gend
+                  ? static_cast<const char*>(p.a) + src_row(p, r) * (int64_t(p.k) * 2)
+                  : nullptr;
+  }
+  const char* wrow[FN];
+  const uint8_t* srow[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    // rows past N re-read the last row: they feed only outputs that are never stored
+    const int64_t n = int64_t(t.g) * p.n + min(t.n0 + 16 * j + lrow, p.n - 1);
+    wrow[j] = static_cast<const char*>(p.w) + n * (p.k / 2);
+    srow[j] = p.w_bscale + n * nblk;
+  }
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c0 = sb0; c0 < sb1; c0 += P) {
+    i32x4_t wv[P][FN];
+    uint32_t sv[P][FN];
+    i32x4_t av[P][FM][4];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int blk = F4_SB_BLOCKS * (c0 + u) + lgrp;
+      const bool in = c0 + u < sb1 && blk < nblk;  // K % 128 == 64: half a super-block
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        wv[u][j] = i32x4_t{0, 0, 0, 0};
+        sv[u][j] = 0;
+        if (in) {
+          wv[u][j] = *reinterpret_cast<const i32x4_t*>(wrow[j] + blk * 16);
+          sv[u][j] = srow[j][blk];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          av[u][i][s] = i32x4_t{0, 0, 0, 0};
+          if (in && arow[i])
+            av[u][i][s] = *reinterpret_cast<const i32x4_t*>(arow[i] + blk * 64 + s * 16);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const float scale = __uint_as_float(sv[u][j] << 23);  // 2^(code - 127)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const i32x4_t b = fp4x8_to_bf16(static_cast<uint32_t>(wv[u][j][s]), scale);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j] = mfma_bf16(av[u][i][s], b, acc[i][j]);
+        }
+      }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) red[wave * UNITS + (i * FN + j) * WAVE + lane] = acc[i][j];
+  __syncthreads();
+  for (int u = threadIdx.x; u < UNITS; u += NW * WAVE) {
+    f32x4_t v = red[u];
+    for (int w = 1; w < NW; ++w) v += red[w * UNITS + u];
+    const int i = u / (FN * WAVE), j = (u / WAVE) % FN, l = u % WAVE;
+    store_block<K_BF16, EPI>(t, v, t.m0 + 16 * i + 4 * (l >> 4), t.n0 + 16 * j + (l & 15));
+  }
+}
+
+template <int EPI>
+hipError_t launch_fp4(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
+                      Timing t) {
+  const dim3 g(grid), b(F4_WAVES * WAVE);
+  if (shape.bm == 16 && shape.bn == 64)
+    return launch_k(gemm_fp4_kernel<16, 64, EPI, F4_WAVES, 2>, g, b, stream, t, p);
+  if (shape.bm == 64 && shape.bn == 32)
+    return launch_k(gemm_fp4_kernel<64, 32, EPI, F4_WAVES, 1>, g, b, stream, t, p);
+  return hipErrorInvalidValue;
+}
+
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
 // Rows up to QV_MAX * 256 columns are read once into registers (all loads in
 // flight together); longer rows are read twice.
@@ -874,6 +1013,8 @@ hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned gri
 
 GemmShape pick_gemm_shape(int kind, int64_t rows, int groups, bool down) {
   const int64_t avg = groups > 0 ? rows / groups : rows;
+  // 4-bit weights: a weight stream for decode; wider M tiles re-read it less
+  if (kind == K_FP4) return avg <= 24 ? GemmShape{16, 64} : GemmShape{64, 32};
   // decode: a weight stream; the up projection (K = hidden) streams best in
   // 64-wide tiles, the down projection (K = inter) in 128-wide ones
   if (avg <= 24) return GemmShape{16, down ? 128 : 64};
@@ -893,6 +1034,9 @@ hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, in
   if (grid64 <= 0) return hipSuccess;
   if (grid64 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>(grid64);
+  if (kind == K_FP4)
+    return epi == EPI_RELU2 ? launch_fp4<EPI_RELU2>(p, shape, grid, stream, t)
+                            : launch_fp4<EPI_PLAIN>(p, shape, grid, stream, t);
   if (kind == K_FP8) return launch_kind<K_FP8>(p, epi, shape, grid, stream, t);
   if (kind == K_BF16) return launch_kind<K_BF16>(p, epi, shape, grid, stream, t);
   return launch_kind<K_F32>(p, epi, shape, grid, stream, t);

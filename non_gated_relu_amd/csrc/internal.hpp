@@ -104,6 +104,7 @@ struct GemmProblem {
   const int32_t* row_index;  // problem row -> index (src = index / index_div), or null
   const void* w;             // [groups, N, K]
   const float* w_scale;      // fp8: [groups, N], else null
+  const uint8_t* w_bscale;   // fp4: E8M0 [groups, N, K/32], else null (w is [groups, N, K/2])
   const int32_t* offsets;    // [groups+1] problem-row offsets, or null: one group
   void* out;                 // [rows, N]
   int64_t a_rows;

@@ -35,7 +35,9 @@ size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int kind_of(int32_t dt) { return dt == MOE_F32 ? K_F32 : dt == MOE_BF16 ? K_BF16 : K_FP8; }
+int kind_of(int32_t dt) {
+  return dt == MOE_F32 ? K_F32 : dt == MOE_BF16 ? K_BF16 : dt == MOE_FP8_E4M3 ? K_FP8 : K_FP4;
+}
 
 size_t esize(int32_t dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
 
@@ -50,12 +52,15 @@ moe_status check_config(const moe_config* c) {
   if (c->top_k < 1 || c->top_k > c->topk_group * eg) return MOE_ERR_INVALID_ARG;
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;
-  const bool dt_ok = (c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32) ||
-                     (c->act_dtype == MOE_BF16 &&
-                      (c->expert_dtype == MOE_BF16 || c->expert_dtype == MOE_FP8_E4M3));
-  const bool dt_known = (c->act_dtype >= 0 && c->act_dtype <= 2) &&
-                        (c->expert_dtype >= 0 && c->expert_dtype <= 2);
-  if (!dt_known) return MOE_ERR_INVALID_ARG;
+  const bool dt_ok = ((c->act_dtype == MOE_F32 && c->expert_dtype == MOE_F32) ||
+                      (c->act_dtype == MOE_BF16 &&
+                       (c->expert_dtype == MOE_BF16 || c->expert_dtype == MOE_FP8_E4M3 ||
+                        c->expert_dtype == MOE_FP4_E2M1))) &&
+                     (c->shared_dtype == c->act_dtype ||
+                      (c->shared_dtype == MOE_FP4_E2M1 && c->expert_dtype == MOE_FP4_E2M1));
+  auto known = [](int32_t dt) { return dt >= MOE_F32 && dt <= MOE_FP4_E2M1; };
+  if (!known(c->act_dtype) || !known(c->expert_dtype) || !known(c->shared_dtype))
+    return MOE_ERR_INVALID_ARG;
   if (!dt_ok) return MOE_ERR_UNSUPPORTED;
   if (c->hidden % 64 || c->inter % 64 || c->shared_inter % 64) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts % 16 || c->n_experts > 256 || c->n_group > 64 || c->top_k > 32)
@@ -103,12 +108,12 @@ struct Mlp {
   const int32_t* row_index = nullptr;
   int index_div = 1;
   const void* w_up = nullptr;
-  const float* up_scale = nullptr;
+  const void* up_scale = nullptr;  // fp8: fp32 per row; fp4: E8M0 per 32 elements
   const void* w_down = nullptr;
-  const float* down_scale = nullptr;
+  const void* down_scale = nullptr;
   float* out = nullptr;
   // workspace
-  void* h = nullptr;        // [rows, inter]: bf16 / fp32 (fp8: fp32 staging)
+  void* h = nullptr;        // [rows, inter]: bf16 (bf16, fp4) / fp32 (fp8: fp32 staging)
   uint8_t* hq = nullptr;    // fp8 codes of h
   float* hs = nullptr;      // fp8 row scales of h
   uint8_t* aq = nullptr;    // fp8 codes of a
@@ -133,7 +138,7 @@ FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats, int64_t extra_rows) 
 }
 
 void carve_mlp_buffers(Carver& cv, Mlp& m, int hidden) {
-  const size_t hsz = m.w_dtype == MOE_BF16 ? 2 : 4;
+  const size_t hsz = m.w_dtype == MOE_BF16 || m.w_dtype == MOE_FP4_E2M1 ? 2 : 4;
   m.h = cv.take<void>(size_t(m.rows) * m.inter * hsz);
   if (m.w_dtype == MOE_FP8_E4M3) {
     m.hq = cv.take<uint8_t>(size_t(m.rows) * m.inter);
@@ -150,7 +155,8 @@ GemmProblem up_problem(const Mlp& m, int hidden) {
   p.a_scale = fp8 ? m.as : nullptr;
   p.row_index = m.row_index;
   p.w = m.w_up;
-  p.w_scale = m.up_scale;
+  p.w_scale = fp8 ? static_cast<const float*>(m.up_scale) : nullptr;
+  p.w_bscale = m.w_dtype == MOE_FP4_E2M1 ? static_cast<const uint8_t*>(m.up_scale) : nullptr;
   p.offsets = m.offsets;
   p.out = m.h;
   p.a_rows = m.a_rows;
@@ -158,7 +164,7 @@ GemmProblem up_problem(const Mlp& m, int hidden) {
   p.n = m.inter;
   p.k = hidden;
   p.index_div = m.index_div;
-  p.out_bf16 = m.w_dtype == MOE_BF16;
+  p.out_bf16 = m.w_dtype == MOE_BF16 || m.w_dtype == MOE_FP4_E2M1;
   return p;
 }
 
@@ -169,7 +175,8 @@ GemmProblem down_problem(const Mlp& m, int hidden) {
   p.a_scale = fp8 ? m.hs : nullptr;
   p.row_index = nullptr;
   p.w = m.w_down;
-  p.w_scale = m.down_scale;
+  p.w_scale = fp8 ? static_cast<const float*>(m.down_scale) : nullptr;
+  p.w_bscale = m.w_dtype == MOE_FP4_E2M1 ? static_cast<const uint8_t*>(m.down_scale) : nullptr;
   p.offsets = m.offsets;
   p.out = m.out;
   p.a_rows = m.rows;
@@ -264,7 +271,7 @@ Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
   Forward f;
   f.T = T;
   f.S = T * c.top_k;
-  f.fused_shared = c.shared_inter > 0 && c.expert_dtype == c.act_dtype;
+  f.fused_shared = c.shared_inter > 0 && c.expert_dtype == c.shared_dtype;
   if (route_mode(T) != ROUTE_ONE_KERNEL) f.logits = cv.take<float>(route_logit_bytes(c, T));
   f.block_counts = cv.take<int32_t>(sizeof(int32_t) * size_t(permute_chunks(f.S)) * c.n_experts);
   f.topk_idx = cv.take<int32_t>(sizeof(int32_t) * size_t(f.S));
@@ -289,7 +296,7 @@ Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
     Mlp& sh = f.shared;
     sh.n_mats = 1;
     sh.inter = c.shared_inter;
-    sh.w_dtype = c.act_dtype;
+    sh.w_dtype = c.shared_dtype;
     sh.a_rows = T;
     sh.rows = T;
     sh.out = cv.take<float>(sizeof(float) * size_t(T) * c.hidden);
@@ -298,7 +305,7 @@ Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
   f.plan = plan_ffn(r.w_dtype, r.rows, r.n_mats, f.fused_shared ? T : 0);
   f.sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.plan.mtiles)));
   if (c.shared_inter > 0 && !f.fused_shared) {
-    const FfnPlan ps = plan_ffn(c.act_dtype, T, 1, 0);
+    const FfnPlan ps = plan_ffn(c.shared_dtype, T, 1, 0);
     f.shared_sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(ps.mtiles)));
   }
   return f;
@@ -346,7 +353,7 @@ size_t carve_standalone(Carver& cv, Mlp& m, int hidden, int32_t** sched) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 1; }
+int32_t moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(moe_status st) {
   switch (st) {
@@ -425,7 +432,7 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!bytes || n_mats < 1 || inter <= 0 || a_rows < 0 || rows < 0) return MOE_ERR_INVALID_ARG;
-  if (w_dtype < 0 || w_dtype > 2) return MOE_ERR_INVALID_ARG;
+  if (w_dtype < MOE_F32 || w_dtype > MOE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
   Carver cv(nullptr);
   Mlp m = standalone_mlp(n_mats, inter, w_dtype, a_rows, nullptr, rows, nullptr, nullptr, 1);
   int32_t* sched;
@@ -436,16 +443,16 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
 moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, int32_t w_dtype,
                           int64_t a_rows, const void* a, int64_t rows,
                           const int32_t* row_offsets, const int32_t* row_index,
-                          int32_t index_div, const void* w_up, const float* w_up_scale,
-                          const void* w_down, const float* w_down_scale, float* out,
+                          int32_t index_div, const void* w_up, const void* w_up_scale,
+                          const void* w_down, const void* w_down_scale, float* out,
                           void* workspace, size_t workspace_bytes, void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (n_mats < 1 || inter <= 0 || a_rows < 0 || rows < 0 || index_div < 1)
     return MOE_ERR_INVALID_ARG;
-  if (w_dtype < 0 || w_dtype > 2) return MOE_ERR_INVALID_ARG;
+  if (w_dtype < MOE_F32 || w_dtype > MOE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
   if (inter % 64) return MOE_ERR_UNSUPPORTED;
-  // fp8 weights take bf16 activations; fp32 weights take fp32; bf16 takes bf16
+  // fp8 and fp4 weights take bf16 activations; fp32 weights take fp32; bf16 takes bf16
   const bool combo = (w_dtype == MOE_F32 && cfg->act_dtype == MOE_F32) ||
                      (w_dtype != MOE_F32 && cfg->act_dtype == MOE_BF16);
   if (!combo) return MOE_ERR_UNSUPPORTED;
@@ -457,7 +464,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, 
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (row_index && !aligned16(row_index)) return MOE_ERR_INVALID_ARG;
-  if (w_dtype == MOE_FP8_E4M3) {
+  if (w_dtype == MOE_FP8_E4M3 || w_dtype == MOE_FP4_E2M1) {
     if (!w_up_scale || !w_down_scale || !aligned16(w_up_scale) || !aligned16(w_down_scale))
       return MOE_ERR_INVALID_ARG;
   }
@@ -496,9 +503,11 @@ moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slo
 
 moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
                              const void* w_gate, const float* e_bias, const void* w_up,
-                             const float* w_up_scale, const void* w_down,
-                             const float* w_down_scale, const void* ws_up, const void* ws_down,
-                             void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                             const void* w_up_scale, const void* w_down,
+                             const void* w_down_scale, const void* ws_up,
+                             const void* ws_up_scale, const void* ws_down,
+                             const void* ws_down_scale, void* y, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* const* ev) {
   moe_status st = check_config(cfg);
@@ -511,8 +520,11 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (c.shared_inter > 0 && (!ws_up || !ws_down || !aligned16(ws_up) || !aligned16(ws_down)))
     return MOE_ERR_INVALID_ARG;
-  if (c.expert_dtype == MOE_FP8_E4M3 &&
+  if ((c.expert_dtype == MOE_FP8_E4M3 || c.expert_dtype == MOE_FP4_E2M1) &&
       (!w_up_scale || !w_down_scale || !aligned16(w_up_scale) || !aligned16(w_down_scale)))
+    return MOE_ERR_INVALID_ARG;
+  if (c.shared_inter > 0 && c.shared_dtype == MOE_FP4_E2M1 &&
+      (!ws_up_scale || !ws_down_scale || !aligned16(ws_up_scale) || !aligned16(ws_down_scale)))
     return MOE_ERR_INVALID_ARG;
   const void* outs[] = {topk_idx, topk_w, expert_counts};
   for (const void* p : outs)
@@ -534,7 +546,9 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
   f.routed.down_scale = w_down_scale;
   f.shared.a = x;
   f.shared.w_up = ws_up;
+  f.shared.up_scale = c.shared_dtype == MOE_FP4_E2M1 ? ws_up_scale : nullptr;
   f.shared.w_down = ws_down;
+  f.shared.down_scale = c.shared_dtype == MOE_FP4_E2M1 ? ws_down_scale : nullptr;
 
   const RouteArgs ra = route_args(c, tokens, x, w_gate, e_bias, idx, wts, f.logits);
   if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
@@ -561,14 +575,14 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
 }
 
 moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
-                       const float* e_bias, const void* w_up, const float* w_up_scale,
-                       const void* w_down, const float* w_down_scale, const void* ws_up,
-                       const void* ws_down, void* y, int32_t* topk_idx, float* topk_w,
-                       int32_t* expert_counts, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       const float* e_bias, const void* w_up, const void* w_up_scale,
+                       const void* w_down, const void* w_down_scale, const void* ws_up,
+                       const void* ws_up_scale, const void* ws_down, const void* ws_down_scale,
+                       void* y, int32_t* topk_idx, float* topk_w, int32_t* expert_counts,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   return moe_forward_timed(cfg, tokens, x, w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
-                           ws_up, ws_down, y, topk_idx, topk_w, expert_counts, workspace,
-                           workspace_bytes, stream, nullptr);
+                           ws_up, ws_up_scale, ws_down, ws_down_scale, y, topk_idx, topk_w,
+                           expert_counts, workspace, workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -12,8 +12,8 @@ import pytest
 
 from non_gated_relu_amd import binding
 from non_gated_relu_amd.binding import (MOE_BF16, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
-                                        MOE_ERR_WORKSPACE, MOE_F32, MOE_FP8_E4M3, MOE_OK,
-                                        MoeConfig)
+                                        MOE_ERR_WORKSPACE, MOE_F32, MOE_FP4_E2M1, MOE_FP8_E4M3,
+                                        MOE_OK, MoeConfig)
 from non_gated_relu_amd.synthetic import WORKLOADS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
-    assert binding.lib().moe_abi_version() == 1
+    assert binding.lib().moe_abi_version() == 2
 
 
 def _cfg(**kw):
@@ -69,8 +69,15 @@ def _ws(cfg, T=32):
     (dict(n_experts=512, n_group=8), MOE_ERR_UNSUPPORTED),
     (dict(act_dtype=MOE_F32), MOE_ERR_UNSUPPORTED),  # fp32 activations with bf16 experts
     (dict(act_dtype=MOE_FP8_E4M3), MOE_ERR_UNSUPPORTED),
+    (dict(shared_dtype=9), MOE_ERR_INVALID_ARG),
+    (dict(shared_dtype=MOE_FP4_E2M1), MOE_ERR_UNSUPPORTED),  # fp4 shared needs fp4 experts
+    (dict(shared_dtype=MOE_FP8_E4M3, expert_dtype=MOE_FP8_E4M3), MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=MOE_FP4_E2M1, act_dtype=MOE_F32, shared_dtype=MOE_F32),
+     MOE_ERR_UNSUPPORTED),
     (dict(), MOE_OK),
     (dict(expert_dtype=MOE_FP8_E4M3), MOE_OK),
+    (dict(expert_dtype=MOE_FP4_E2M1), MOE_OK),
+    (dict(expert_dtype=MOE_FP4_E2M1, shared_dtype=MOE_FP4_E2M1), MOE_OK),
 ])
 def test_config_checks(kw, status):
     assert _ws(_cfg(**kw))[0] == status
@@ -94,7 +101,7 @@ def test_zero_tokens_enqueue_nothing():
     L = binding.lib()
     c = _cfg()
     assert L.moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, 0, None) == MOE_OK
-    assert L.moe_forward(ctypes.byref(c), 0, *([None] * 14), 0, None) == MOE_OK
+    assert L.moe_forward(ctypes.byref(c), 0, *([None] * 16), 0, None) == MOE_OK
     assert L.moe_combine(ctypes.byref(c), 0, None, None, None, None, None, None) == MOE_OK
 
 
@@ -109,13 +116,21 @@ def test_null_and_misaligned_pointers_are_refused():
                        None) == MOE_ERR_INVALID_ARG
     args = [fake] * 6 + [None] * 2 + [fake] * 2 + [fake]
     # x, w_gate, e_bias, w_up, w_up_scale(NULL ok for bf16), ...
-    st = L.moe_forward(ctypes.byref(c), 4, fake, fake, fake, fake, None, fake, None, fake, fake,
-                       fake, None, None, None, None, 0, None)
+    st = L.moe_forward(ctypes.byref(c), 4, fake, fake, fake, fake, None, fake, None, fake, None,
+                       fake, None, fake, None, None, None, None, 0, None)
     assert st == MOE_ERR_WORKSPACE
     c8 = _cfg(expert_dtype=MOE_FP8_E4M3)
-    st = L.moe_forward(ctypes.byref(c8), 4, fake, fake, fake, fake, None, fake, None, fake, fake,
-                       fake, None, None, None, fake, 1 << 40, None)
+    st = L.moe_forward(ctypes.byref(c8), 4, fake, fake, fake, fake, None, fake, None, fake, None,
+                       fake, None, fake, None, None, None, fake, 1 << 40, None)
     assert st == MOE_ERR_INVALID_ARG  # fp8 weights need their scales
+    c4 = _cfg(expert_dtype=MOE_FP4_E2M1)
+    st = L.moe_forward(ctypes.byref(c4), 4, fake, fake, fake, fake, None, fake, None, fake, None,
+                       fake, None, fake, None, None, None, fake, 1 << 40, None)
+    assert st == MOE_ERR_INVALID_ARG  # fp4 weights need their block scales
+    c44 = _cfg(expert_dtype=MOE_FP4_E2M1, shared_dtype=MOE_FP4_E2M1)
+    st = L.moe_forward(ctypes.byref(c44), 4, fake, fake, fake, fake, fake, fake, fake, fake, None,
+                       fake, None, fake, None, None, None, fake, 1 << 40, None)
+    assert st == MOE_ERR_INVALID_ARG  # and so does an fp4 shared expert
     del args
 
 
@@ -148,6 +163,13 @@ def test_expert_ffn_checks():
     st = L.moe_expert_ffn(ctypes.byref(c), 4, 128, MOE_BF16, 8, fake, 0, fake, None, 1, fake, None,
                           fake, None, fake, fake, 16, None)
     assert st == MOE_OK
+    # fp4 weights need their block scales; unknown weight types are refused
+    st = L.moe_expert_ffn(ctypes.byref(c), 4, 128, MOE_FP4_E2M1, 8, fake, 8, fake, None, 1, fake,
+                          None, fake, fake, fake, fake, 1 << 30, None)
+    assert st == MOE_ERR_INVALID_ARG
+    st = L.moe_expert_ffn(ctypes.byref(c), 4, 128, 4, 8, fake, 8, fake, None, 1, fake, fake,
+                          fake, fake, fake, fake, 1 << 30, None)
+    assert st == MOE_ERR_INVALID_ARG
 
 
 def test_status_strings():
@@ -161,7 +183,9 @@ def test_status_strings():
 
 
 def test_config_struct_layout_matches_header():
-    # 8 int32 + float + 2 int32
-    assert ctypes.sizeof(MoeConfig) == 44
+    # 8 int32 + float + 3 int32
+    assert ctypes.sizeof(MoeConfig) == 48
     c = binding.config_from(WORKLOADS["fp8-T8192"])
-    assert (c.act_dtype, c.expert_dtype) == (MOE_BF16, MOE_FP8_E4M3)
+    assert (c.act_dtype, c.expert_dtype, c.shared_dtype) == (MOE_BF16, MOE_FP8_E4M3, MOE_BF16)
+    c = binding.config_from(WORKLOADS["decode-fp4-T32"])
+    assert (c.act_dtype, c.expert_dtype, c.shared_dtype) == (MOE_BF16, MOE_FP4_E2M1, MOE_FP4_E2M1)

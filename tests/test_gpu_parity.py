@@ -30,9 +30,20 @@ BIG_GROUPS_BF16 = Workload("big-groups-bf16-T1024", 1024, 256, 16, 4, 1, 2, 320,
 BIG_GROUPS_FP8 = Workload("big-groups-fp8-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp8",
                           seed=28)
 SHORT_K = Workload("big-groups-bf16-d64", 1024, 64, 16, 4, 1, 2, 128, 64, "bf16", "bf16", seed=29)
+# 4-bit experts: K = 192 and 320 end in half a 128-element super-block; the
+# shared expert is fp4 (one launch with the routed experts) or bf16 (its own).
+RAGGED_FP4 = Workload("ragged-fp4-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "fp4", seed=30,
+                      shared_dtype="fp4")
+FP4_BF16_SHARED = Workload("fp4-bf16-shared-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "fp4",
+                           seed=31)
+FP4_MANY_ROWS = Workload("many-rows-fp4-T600", 600, 128, 16, 2, 1, 2, 128, 192, "bf16", "fp4",
+                         seed=32, shared_dtype="fp4")
+BIG_GROUPS_FP4 = Workload("big-groups-fp4-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp4",
+                          seed=33, shared_dtype="fp4")
 
 SMALL = [WORKLOADS["tiny-f32-T64"], RAGGED_BF16, RAGGED_FP8, PLAIN_TOPK, ALL_GROUPS, WHOLE_GROUP,
-         BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE, BIG_GROUPS_BF16, BIG_GROUPS_FP8, SHORT_K]
+         BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE, BIG_GROUPS_BF16, BIG_GROUPS_FP8, SHORT_K,
+         RAGGED_FP4, FP4_BF16_SHARED, FP4_MANY_ROWS, WORKLOADS["decode-fp4-T32"]]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,19 +58,49 @@ def _tol(wl):
     return dict(max_tol=1e-4, mean_tol=1e-5) if wl.act_dtype == "f32" else {}
 
 
+def _scales(d, wl, shared=False):
+    """(up, down) scale arrays of the routed (or shared) weights in d, or Nones:
+    fp32 per-row scales for fp8, E8M0 block scales for fp4."""
+    dt = wl.shared_weight_dtype if shared else wl.expert_dtype
+    pre = "ws_" if shared else "w_"
+    key = {"fp8": "_scale", "fp4": "_bscale"}.get(dt)
+    if key is None:
+        return None, None
+    up, down = d.get(pre + "up" + key), d.get(pre + "down" + key)
+    return (up[None], down[None]) if shared else (up, down)
+
+
+def _zero_some_fp4_blocks(inp, wl):
+    """All-zero 32-element blocks with scale code 0, as the quantiser writes
+    for all-zero weights: a few in the routed and shared matrices."""
+    rng = np.random.default_rng(5)
+    names = [("w_up", "w_up_bscale"), ("w_down", "w_down_bscale")]
+    if wl.shared_weight_dtype == "fp4" and wl.shared_inter:
+        names += [("ws_up", "ws_up_bscale"), ("ws_down", "ws_down_bscale")]
+    for w, b in names:
+        sc = inp[b].reshape(-1, inp[b].shape[-1])
+        codes = inp[w].reshape(-1, inp[w].shape[-1])
+        for _ in range(8):
+            r, blk = rng.integers(sc.shape[0]), rng.integers(sc.shape[1])
+            sc[r, blk] = 0
+            codes[r, 16 * blk:16 * blk + 16] = 0
+
+
 def _layer_parts(wl, t, cfg):
     T = t["x"].shape[0]
     idx, w = binding.route(cfg, t["x"], t["w_gate"], t["e_bias"])
     perm = binding.permute(cfg, idx, t["x"], with_x_perm=True)
+    su, sd = _scales(t, wl)
     y_perm = binding.expert_ffn(cfg, t["w_up"], t["w_down"], t["x"], perm["offsets"], T * wl.top_k,
                                 row_index=perm["sorted_slot"], index_div=wl.top_k,
-                                w_dtype=wl.expert_dtype, w_up_scale=t.get("w_up_scale"),
-                                w_down_scale=t.get("w_down_scale"))
+                                w_dtype=wl.expert_dtype, w_up_scale=su, w_down_scale=sd)
     shared = None
     if wl.shared_inter:
         off = torch.tensor([0, T], dtype=torch.int32, device=t["x"].device)
+        su, sd = _scales(t, wl, shared=True)
         shared = binding.expert_ffn(cfg, t["ws_up"][None], t["ws_down"][None], t["x"], off, T,
-                                    w_dtype=wl.act_dtype)
+                                    w_dtype=wl.shared_weight_dtype, w_up_scale=su,
+                                    w_down_scale=sd)
     y = binding.combine(cfg, perm["slot_pos"], w, y_perm, shared)
     return dict(idx=idx, w=w, perm=perm, y_perm=y_perm, shared=shared, y=y)
 
@@ -68,6 +109,8 @@ def _layer_parts(wl, t, cfg):
 def test_small_layer_every_entry_point(wl):
     print(f"case {wl.name}", flush=True)
     inp = make_inputs(wl)
+    if wl.expert_dtype == "fp4":
+        _zero_some_fp4_blocks(inp, wl)
     t = upload(inp, wl)
     cfg = binding.config_from(wl)
     ref = oracle.forward(wl, inp)
@@ -94,7 +137,8 @@ def test_small_layer_every_entry_point(wl):
     mats = parts["idx"].cpu().numpy().reshape(-1)[sorted_slot]
     ffn_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, rows, mats, inp["w_up"], inp["w_down"],
                               wl.expert_dtype, inp["w_up_scale"], inp["w_down_scale"],
-                              quant_a=wl.expert_dtype == "fp8")
+                              quant_a=wl.expert_dtype == "fp8", w_up_bscale=inp["w_up_bscale"],
+                              w_down_bscale=inp["w_down_bscale"])
     allow_rows = allow_tok = None
     if wl.expert_dtype == "fp8":
         allow_rows = fp8_flips.row_allowance(inp["x"], rows, mats, inp["w_up"], inp["w_up_scale"],
@@ -104,8 +148,10 @@ def test_small_layer_every_entry_point(wl):
     assert_close_rms(to_f64(parts["y_perm"]), ffn_ref, f"{wl.name} expert_ffn", **_tol(wl),
                      row_allow=allow_rows)
     if wl.shared_inter:
+        bu, bd = _scales(inp, wl, shared=True)
         sh_ref = oracle.ffn_rows(inp["x"], wl.act_dtype, np.arange(T), np.zeros(T),
-                                 inp["ws_up"][None], inp["ws_down"][None], wl.act_dtype)
+                                 inp["ws_up"][None], inp["ws_down"][None], wl.shared_weight_dtype,
+                                 w_up_bscale=bu, w_down_bscale=bd)
         assert_close_rms(to_f64(parts["shared"]), sh_ref, f"{wl.name} shared", **_tol(wl))
     # combine: only the final rounding separates it from the fp64 sum of its inputs
     comb_ref = oracle.combine(parts["w"].cpu().numpy(), to_f64(parts["y_perm"]), slot_pos,
@@ -117,9 +163,11 @@ def test_small_layer_every_entry_point(wl):
     assert_close_rms(got, ref["y"], f"{wl.name} layer", **_tol(wl), row_allow=allow_tok)
 
     # the fused entry point equals the composition bit for bit
+    su, sd = _scales(t, wl)
+    ssu, ssd = t.get("ws_up_bscale"), t.get("ws_down_bscale")
     y = binding.forward(cfg, t["x"], t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
-                        t.get("ws_up"), t.get("ws_down"), t.get("w_up_scale"),
-                        t.get("w_down_scale"))
+                        t.get("ws_up"), t.get("ws_down"), su, sd, ws_up_scale=ssu,
+                        ws_down_scale=ssd)
     torch.cuda.synchronize()
     assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
                        parts["y"].view(torch.int16) if y.dtype == torch.bfloat16 else parts["y"])
@@ -129,7 +177,7 @@ def _bits(y):
     return y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)
 
 
-@pytest.mark.parametrize("wl", [RAGGED_BF16, RAGGED_FP8, WORKLOADS["tiny-f32-T64"]],
+@pytest.mark.parametrize("wl", [RAGGED_BF16, RAGGED_FP8, WORKLOADS["tiny-f32-T64"], RAGGED_FP4],
                          ids=lambda w: w.name)
 def test_deterministic_and_token_permutation_equivariant(wl):
     inp = make_inputs(wl)
@@ -218,7 +266,8 @@ def test_identical_experts_reduce_to_one_dense_mlp():
     assert_close_rms(to_f64(y), 2.5 * ffn + sh, "identical experts")
 
 
-@pytest.mark.parametrize("wl", [WORKLOADS["decode-bf16-T32"], RAGGED_FP8], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [WORKLOADS["decode-bf16-T32"], RAGGED_FP8,
+                                WORKLOADS["decode-fp4-T32"]], ids=lambda w: w.name)
 def test_graph_replays_match_eager(wl):
     # every replay is checked, with eager work and synchronisations between them
     inp = make_inputs(wl)
@@ -246,7 +295,8 @@ def test_graph_replays_match_eager(wl):
     del other
 
 
-@pytest.mark.parametrize("wl", [BIG_GROUPS_BF16, BIG_GROUPS_FP8], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [BIG_GROUPS_BF16, BIG_GROUPS_FP8, BIG_GROUPS_FP4],
+                         ids=lambda w: w.name)
 def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
     """A row's result is the same whichever tile shape computes it: a call
     with hundreds of rows per expert (256-row tiles) and a call with a few
@@ -258,8 +308,9 @@ def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
     T = wl.tokens
     rng = np.random.default_rng(7)
     src = torch.from_numpy(rng.integers(0, T, size=1200).astype(np.int32)).cuda()
-    sc = dict(w_dtype=wl.expert_dtype, w_up_scale=t.get("w_up_scale"),
-              w_down_scale=t.get("w_down_scale"))
+    su, sd = _scales(t, wl)
+    sc = dict(w_dtype=wl.expert_dtype, w_up_scale=None if su is None else su[:2],
+              w_down_scale=None if sd is None else sd[:2])
     big_off = torch.tensor([0, 700, 1200], dtype=torch.int32, device="cuda")
     big = binding.expert_ffn(cfg, t["w_up"][:2], t["w_down"][:2], t["x"], big_off, 1200,
                              row_index=src, **sc)
@@ -270,11 +321,13 @@ def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
     torch.cuda.synchronize()
     assert torch.equal(big[pick], small)
     mats = np.repeat([0, 1], [700, 500])
+    bu, bd = _scales(inp, wl)
+    fp8 = wl.expert_dtype == "fp8"
     ref = oracle.ffn_rows(inp["x"], wl.act_dtype, src.cpu().numpy(), mats, inp["w_up"][:2],
                           inp["w_down"][:2], wl.expert_dtype,
-                          None if inp["w_up_scale"] is None else inp["w_up_scale"][:2],
-                          None if inp["w_down_scale"] is None else inp["w_down_scale"][:2],
-                          quant_a=wl.expert_dtype == "fp8")
+                          bu[:2] if fp8 else None, bd[:2] if fp8 else None, quant_a=fp8,
+                          w_up_bscale=None if fp8 or bu is None else bu[:2],
+                          w_down_bscale=None if fp8 or bd is None else bd[:2])
     allow = None
     if wl.expert_dtype == "fp8":
         allow = fp8_flips.row_allowance(inp["x"], src.cpu().numpy(), mats, inp["w_up"],
