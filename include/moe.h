@@ -85,11 +85,12 @@ typedef struct moe_config {
   float routed_scaling_factor;
   int32_t act_dtype;     /* MOE_F32 or MOE_BF16: x, w_gate, y                        */
   int32_t expert_dtype;  /* routed weights: MOE_F32 (needs act F32), MOE_BF16,
-                            MOE_FP8_E4M3 or MOE_FP4_E2M1 (these need act BF16)       */
+                            MOE_FP8_E4M3 or MOE_FP4_E2M1 (these need act BF16;
+                            fp4 also needs d and I <= 8192)                          */
   int32_t shared_dtype;  /* shared-expert weights: act_dtype, or MOE_FP4_E2M1 when
                             expert_dtype is MOE_FP4_E2M1 (the 4-bit checkpoint of
                             vllm.cpp PR "spec(MODEL-TEXT-nemotron-h)" quantises the
-                            shared experts with the routed ones)                    */
+                            shared experts with the routed ones; fp4: Is <= 8192)   */
 } moe_config;
 
 /* Bytes of workspace moe_forward needs for `tokens` tokens (host output). The
@@ -145,7 +146,10 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
  *   w_up_scale, w_down_scale
  *                MOE_FP8_E4M3: fp32 per-row scales [n_mats, inter] and [n_mats, d];
  *                MOE_FP4_E2M1: E8M0 block scales (uint8) [n_mats, inter, d/32]
- *                and [n_mats, d, inter/32], codes 0..254;
+ *                and [n_mats, d, inter/32], codes 1..252 (every weight a
+ *                normal bf16 value); code 0 only for all-zero blocks.  fp4
+ *                also needs a_rows*d*2 and rows*inter*2 below 2^31 and
+ *                d, inter <= 8192 (else MOE_ERR_UNSUPPORTED)
  *                otherwise NULL (ignored)
  *   out          [rows, d] fp32
  * With fp8 weights each a row is quantised per row to e4m3 (scale amax/448,

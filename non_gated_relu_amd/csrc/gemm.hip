@@ -757,24 +757,36 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
 // ------------------------------------------------------------ fp4 kernel
 //
 // MXFP4 weights (an e2m1 code times the E8M0 power of two of its 32-element
-// block) with bf16 activations.  In decode each weight byte feeds one MFMA
-// or a few, so the launch is a weight stream: the codes go from global
-// memory straight into registers, 16 bytes (one scale block of one row) per
-// lane, and are widened where the fragment is built by
-// v_cvt_scalef32_pk_bf16_fp4, which applies the block's power of two.  An
-// e2m1 value times a power of two is a bf16 value, so the MFMA sees the
-// dequantised weight exactly.
+// block) with bf16 activations.  Codes are widened where an MFMA fragment is
+// built, by v_cvt_scalef32_pk_bf16_fp4, which applies the block's power of
+// two; an e2m1 value times a power of two is a bf16 value, so the bf16 MFMA
+// sees the dequantised weight exactly.
 //
-// The NW waves of a workgroup split K: wave w takes a contiguous run of
-// 128-element super-blocks.  In super-block b, lane group g (lanes 16 g ..
-// 16 g + 15, one per row) owns scale block 4 b + g, and MFMA step s (0..3)
-// gives every lane elements 8 s .. 8 s + 7 of its own block, of the
-// activation row and of the weight row alike; the four steps cover the 128
-// elements once.  The waves' partial tiles are then summed through LDS in
-// wave order (a fixed order, so results are deterministic) and stored by the
-// usual epilogue.  A rows past the group end are never read.
-constexpr int F4_SB_BLOCKS = 4;  // 32-element scale blocks per super-block
-constexpr int F4_WAVES = 8;
+// A workgroup of four waves owns a (16 FM) x 64 output tile; each wave owns
+// 16 weight rows and all FM 16-row fragments of the activations.  K streams
+// through LDS in 256-element stages, double buffered, with the loads of the
+// next D stages in registers.  Every load is a buffer load issued
+// unconditionally: what lies past K, past the group's rows or past the last
+// stage is out of the buffer's range and reads as zero without touching
+// memory, so the number of loads in flight is the same on every path and the
+// waits are exact.  A stage row of codes is 128 bytes, one whole cache line,
+// read by 8 consecutive lanes; the activation stage (16 FM rows of 512
+// bytes) is shared by the four waves.
+//
+// Element order inside a stage: in super-block h (128 elements, h = 0, 1)
+// lane group g (lanes 16 g .. 16 g + 15) owns scale block 4 h + g, and MFMA
+// step s (0..3) gives every lane elements 8 s .. 8 s + 7 of its own block, of
+// the activation row and of the weight row alike; the four steps cover the
+// super-block once.  A lane's codes for a super-block are one 16-byte LDS
+// read and one scale.  Each output element is one MFMA chain over the
+// super-blocks and steps in ascending order whatever FM is, so the tile
+// shape does not change results.  The tile's block scales (64 rows x K/32
+// bytes, contiguous) sit in dynamic LDS sized to K.
+constexpr int F4_BN = 64;
+constexpr int F4_KE = 256;         // K elements per stage
+constexpr int F4_WROW = 128 + 16;  // LDS bytes per weight row (padded)
+constexpr int F4_AROW = 512 + 16;  // LDS bytes per activation row (padded)
+constexpr uint32_t F4_OOB = 0x80000000u;  // a buffer offset past every range here
 
 __device__ __forceinline__ i32x4_t fp4x8_to_bf16(uint32_t codes, float scale) {
   i32x4_t r;
@@ -785,110 +797,157 @@ __device__ __forceinline__ i32x4_t fp4x8_to_bf16(uint32_t codes, float scale) {
   return r;
 }
 
-// P super-blocks of loads are issued together before their MFMAs.
-template <int BM, int BN, int EPI, int NW, int P>
-__global__ __launch_bounds__(NW * WAVE) void gemm_fp4_kernel(GemmArgs pa) {
-  constexpr int FM = BM / 16, FN = BN / 16;
-  constexpr int UNITS = FM * FN * WAVE;  // f32x4 partial results per wave
-  __shared__ f32x4_t red[NW * UNITS];
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t f4_rsrc(const void* base, uint32_t bytes) {
+  // raw buffer, no swizzle; offsets at or past `bytes` read as zero
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+template <int EPI, int D, int FM>
+__global__ __launch_bounds__(256) void gemm_fp4_kernel(GemmArgs pa) {
+  constexpr int BM = 16 * FM, BN = F4_BN;
+  constexpr int AQ = 2 * FM;  // activation chunks per thread and stage
+  constexpr int WSZ = BN * F4_WROW;
+  constexpr int STAGE = WSZ + BM * F4_AROW;
+  constexpr int SC_PT = F4_SCALE_LDS / 16 / 256;
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  extern __shared__ __attribute__((aligned(16))) uint8_t scl[];
 
   Tile t;
   if (!locate_tile<BM, BN>(pa, t, blockIdx.x)) return;
   const GemmProblem& p = t.p;
-  const int wave = threadIdx.x / WAVE;
+  const int tid = threadIdx.x;
+  const int wave = tid / WAVE;
   const int lane = lane_id();
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
-  const int nblk = p.k / 32;  // scale blocks per row (the host guarantees K % 64 == 0)
-  const int nsb = (nblk + F4_SB_BLOCKS - 1) / F4_SB_BLOCKS;
-  const int sb0 = wave * nsb / NW;
-  const int sb1 = (wave + 1) * nsb / NW;
+  const int nblk = p.k / 32;  // the host guarantees K % 64 == 0
+  const uint32_t wbytes = p.k / 2;
+  const uint32_t abytes = p.k * 2;
+  const int nst = (p.k + F4_KE - 1) / F4_KE;
 
-  const char* arow[FM];
+  // weights and scales of the tile (N % 64 == 0: the tile is whole)
+  const int sc_bytes = BN * nblk;
+  const int64_t row0 = int64_t(t.g) * p.n + t.n0;
+  const __amdgpu_buffer_rsrc_t wr = f4_rsrc(static_cast<const char*>(p.w) + row0 * wbytes,
+                                            BN * wbytes);
+  const __amdgpu_buffer_rsrc_t sr = f4_rsrc(p.w_bscale + row0 * nblk, sc_bytes);
+  i32x4_t scv[SC_PT];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t r = t.m0 + 16 * i + lrow;
-    arow[i] = r < t.gend
-                  ? static_cast<const char*>(p.a) + src_row(p, r) * (int64_t(p.k) * 2)
-                  : nullptr;
+  for (int q = 0; q < SC_PT; ++q)
+    scv[q] = __builtin_amdgcn_raw_buffer_load_b128(sr, (tid + q * 256) * 16, 0, 0);
+
+  // this thread's chunks: weight rows tid / 8 + 32 q at byte (tid % 8) * 16
+  // of the stage; activation rows tid / 32 + 8 q at byte (tid % 32) * 16
+  const uint32_t wc = (tid % 8) * 16;
+  const uint32_t ac = (tid % 32) * 16;
+  uint32_t wbase[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) wbase[q] = (tid / 8 + 32 * q) * wbytes;
+  struct Regs {
+    i32x4_t w[2], a[AQ];
+  };
+  Regs R[D];
+  auto gload_w = [&](int st, Regs& r) {
+    const uint32_t k = st * 128 + wc;  // past K or past the last stage: zero
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      r.w[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, k < wbytes ? wbase[q] + k : F4_OOB, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) gload_w(d, R[d]);  // the weights do not wait for the rows
+
+  // (the host keeps a_rows * K * 2 below 2^31 for fp4 weights)
+  const int64_t a_all = p.a_rows * int64_t(abytes);
+  const uint32_t a_range = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(a_all > 0x7fffffff ? 0x7fffffff : a_all));
+  const __amdgpu_buffer_rsrc_t ar = f4_rsrc(p.a, a_range);
+  // row starts of this thread's activation rows; past the group end the
+  // start is F4_OOB, so every offset from it is out of range too
+  uint32_t abase[AQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int64_t r = t.m0 + tid / 32 + 8 * q;
+    abase[q] = r < t.gend ? static_cast<uint32_t>(src_row(p, r) * abytes) : F4_OOB;
   }
-  const char* wrow[FN];
-  const uint8_t* srow[FN];
+  auto gload_a = [&](int st, Regs& r) {
+    const uint32_t k = st * 512 + ac;  // past K or past the last stage: zero
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    // rows past N re-read the last row: they feed only outputs that are never stored
-    const int64_t n = int64_t(t.g) * p.n + min(t.n0 + 16 * j + lrow, p.n - 1);
-    wrow[j] = static_cast<const char*>(p.w) + n * (p.k / 2);
-    srow[j] = p.w_bscale + n * nblk;
+    for (int q = 0; q < AQ; ++q)
+      r.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, k < abytes ? abase[q] + k : F4_OOB, 0, 0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) gload_a(d, R[d]);
+  auto sstore = [&](int buf, const Regs& r) {
+    char* ws = smem + buf * STAGE;
+    char* as = ws + WSZ;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<i32x4_t*>(ws + (tid / 8 + 32 * q) * F4_WROW + wc) = r.w[q];
+#pragma unroll
+    for (int q = 0; q < AQ; ++q)
+      *reinterpret_cast<i32x4_t*>(as + (tid / 32 + 8 * q) * F4_AROW + ac) = r.a[q];
+  };
+#pragma unroll
+  for (int q = 0; q < SC_PT; ++q) {
+    const int off = (tid + q * 256) * 16;
+    if (off < sc_bytes) *reinterpret_cast<i32x4_t*>(scl + off) = scv[q];
   }
-
-  f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int c0 = sb0; c0 < sb1; c0 += P) {
-    i32x4_t wv[P][FN];
-    uint32_t sv[P][FN];
-    i32x4_t av[P][FM][4];
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int blk = F4_SB_BLOCKS * (c0 + u) + lgrp;
-      const bool in = c0 + u < sb1 && blk < nblk;  // K % 128 == 64: half a super-block
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        wv[u][j] = i32x4_t{0, 0, 0, 0};
-        sv[u][j] = 0;
-        if (in) {
-          wv[u][j] = *reinterpret_cast<const i32x4_t*>(wrow[j] + blk * 16);
-          sv[u][j] = srow[j][blk];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          av[u][i][s] = i32x4_t{0, 0, 0, 0};
-          if (in && arow[i])
-            av[u][i][s] = *reinterpret_cast<const i32x4_t*>(arow[i] + blk * 64 + s * 16);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < P; ++u)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const float scale = __uint_as_float(sv[u][j] << 23);  // 2^(code - 127)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const i32x4_t b = fp4x8_to_bf16(static_cast<uint32_t>(wv[u][j][s]), scale);
-#pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][j] = mfma_bf16(av[u][i][s], b, acc[i][j]);
-        }
-      }
-  }
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) red[wave * UNITS + (i * FN + j) * WAVE + lane] = acc[i][j];
+  sstore(0, R[0]);
   __syncthreads();
-  for (int u = threadIdx.x; u < UNITS; u += NW * WAVE) {
-    f32x4_t v = red[u];
-    for (int w = 1; w < NW; ++w) v += red[w * UNITS + u];
-    const int i = u / (FN * WAVE), j = (u / WAVE) % FN, l = u % WAVE;
-    store_block<K_BF16, EPI>(t, v, t.m0 + 16 * i + 4 * (l >> 4), t.n0 + 16 * j + (l & 15));
+
+  f32x4_t acc[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint8_t* my_scl = scl + (16 * wave + lrow) * nblk;
+  for (int st0 = 0; st0 < nst; st0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int st = st0 + d;
+      if (st >= nst) break;
+      // R[d] held stage st (stored last step); it now takes stage st + D
+      gload_w(st + D, R[d]);
+      gload_a(st + D, R[d]);
+      const char* ws = smem + (st & 1) * STAGE + (16 * wave + lrow) * F4_WROW + 16 * lgrp;
+      const char* as = smem + (st & 1) * STAGE + WSZ + lrow * F4_AROW + 64 * lgrp;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int blk = 8 * st + 4 * h + lgrp;
+        const uint32_t c = my_scl[min(blk, nblk - 1)];
+        const uint32_t code = blk < nblk ? c : 0u;        // past K: zero codes anyway
+        const float scale = __uint_as_float(code << 23);  // 2^(code - 127)
+        const i32x4_t w = *reinterpret_cast<const i32x4_t*>(ws + 64 * h);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const i32x4_t b = fp4x8_to_bf16(static_cast<uint32_t>(w[s]), scale);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const i32x4_t a =
+                *reinterpret_cast<const i32x4_t*>(as + 16 * i * F4_AROW + 256 * h + 16 * s);
+            acc[i] = mfma_bf16(a, b, acc[i]);
+          }
+        }
+      }
+      if (st + 1 < nst) sstore((st + 1) & 1, R[(d + 1) % D]);
+      __syncthreads();
+    }
   }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    store_block<K_BF16, EPI>(t, acc[i], t.m0 + 16 * i + 4 * lgrp, t.n0 + 16 * wave + lrow);
 }
 
 template <int EPI>
 hipError_t launch_fp4(const GemmArgs& p, GemmShape shape, unsigned grid, hipStream_t stream,
                       Timing t) {
-  const dim3 g(grid), b(F4_WAVES * WAVE);
-  if (shape.bm == 16 && shape.bn == 64)
-    return launch_k(gemm_fp4_kernel<16, 64, EPI, F4_WAVES, 2>, g, b, stream, t, p);
-  if (shape.bm == 64 && shape.bn == 32)
-    return launch_k(gemm_fp4_kernel<64, 32, EPI, F4_WAVES, 1>, g, b, stream, t, p);
+  // dynamic LDS: the block scales of a tile, for the larger K of the problems
+  const int kmax = std::max(p.prob[0].k, p.prob[1].w ? p.prob[1].k : 0);
+  const unsigned shm = static_cast<unsigned>((F4_BN * (kmax / 32) + 15) / 16 * 16);
+  const dim3 g(grid), b(256);
+  if (shape.bn != F4_BN) return hipErrorInvalidValue;
+  // decode tiles: two stages in flight; 64-row tiles: one (registers)
+  if (shape.bm == 16) return launch_k_shm(gemm_fp4_kernel<EPI, 2, 1>, g, b, shm, stream, t, p);
+  if (shape.bm == 64) return launch_k_shm(gemm_fp4_kernel<EPI, 1, 4>, g, b, shm, stream, t, p);
   return hipErrorInvalidValue;
 }
 
@@ -1014,7 +1073,7 @@ hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned gri
 GemmShape pick_gemm_shape(int kind, int64_t rows, int groups, bool down) {
   const int64_t avg = groups > 0 ? rows / groups : rows;
   // 4-bit weights: a weight stream for decode; wider M tiles re-read it less
-  if (kind == K_FP4) return avg <= 24 ? GemmShape{16, 64} : GemmShape{64, 32};
+  if (kind == K_FP4) return GemmShape{avg <= 24 ? 16 : 64, 64};
   // decode: a weight stream; the up projection (K = hidden) streams best in
   // 64-wide tiles, the down projection (K = inter) in 128-wide ones
   if (avg <= 24) return GemmShape{16, down ? 128 : 64};

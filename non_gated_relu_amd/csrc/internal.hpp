@@ -24,6 +24,17 @@ inline hipError_t launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipS
   return hipGetLastError();
 }
 
+// launch_k with `shm` bytes of dynamic LDS.
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_k_shm(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned shm,
+                               hipStream_t s, Timing t, Args... args) {
+  if (t.start || t.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, t.start, t.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  return hipGetLastError();
+}
+
 struct RouteArgs {
   const void* x;        // [tokens, d]
   const void* w_gate;   // [E, d]
@@ -131,6 +142,11 @@ struct QuantArgs {
   int cols;
   int in_bf16;
 };
+
+// Block scales of one fp4 weight tile are staged in LDS: BN rows x K/32
+// bytes must fit, which bounds K of fp4 weights (hidden, inter, shared_inter).
+constexpr int F4_SCALE_LDS = 16384;
+constexpr int F4_MAX_K = F4_SCALE_LDS * 32 / 64;
 
 // Tile shape of a grouped GEMM launch.  `stream` asks for the DMA-ring
 // kernel of thin tiles (bf16, bm = 16), which keeps more bytes in flight but

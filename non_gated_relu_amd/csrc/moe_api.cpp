@@ -65,12 +65,27 @@ moe_status check_config(const moe_config* c) {
   if (c->hidden % 64 || c->inter % 64 || c->shared_inter % 64) return MOE_ERR_UNSUPPORTED;
   if (c->n_experts % 16 || c->n_experts > 256 || c->n_group > 64 || c->top_k > 32)
     return MOE_ERR_UNSUPPORTED;
+  if (c->expert_dtype == MOE_FP4_E2M1 && (c->hidden > F4_MAX_K || c->inter > F4_MAX_K))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->shared_dtype == MOE_FP4_E2M1 && c->shared_inter > F4_MAX_K) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// fp4 weights: the GEMM addresses its activation and h rows with 32-bit
+// buffer offsets, so [a_rows, K] bf16 operands must stay below 2 GiB.
+bool fp4_rows_fit(int64_t a_rows, int64_t a_cols, int64_t h_rows, int64_t h_cols) {
+  constexpr int64_t LIM = 0x7fffffff;
+  return a_rows * a_cols * 2 <= LIM && h_rows * h_cols * 2 <= LIM;
 }
 
 moe_status check_tokens(const moe_config* c, int64_t tokens) {
   if (tokens < 0) return MOE_ERR_INVALID_ARG;
   if (tokens * c->top_k >= (int64_t(1) << 31) - 1) return MOE_ERR_UNSUPPORTED;
+  if (c->expert_dtype == MOE_FP4_E2M1 &&
+      !fp4_rows_fit(tokens, c->hidden, tokens * c->top_k, c->inter))
+    return MOE_ERR_UNSUPPORTED;
+  if (c->shared_dtype == MOE_FP4_E2M1 && !fp4_rows_fit(tokens, c->hidden, tokens, c->shared_inter))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -433,6 +448,7 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
   if (st != MOE_OK) return st;
   if (!bytes || n_mats < 1 || inter <= 0 || a_rows < 0 || rows < 0) return MOE_ERR_INVALID_ARG;
   if (w_dtype < MOE_F32 || w_dtype > MOE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
+  if (w_dtype == MOE_FP4_E2M1 && inter > F4_MAX_K) return MOE_ERR_UNSUPPORTED;
   Carver cv(nullptr);
   Mlp m = standalone_mlp(n_mats, inter, w_dtype, a_rows, nullptr, rows, nullptr, nullptr, 1);
   int32_t* sched;
@@ -452,6 +468,9 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, 
     return MOE_ERR_INVALID_ARG;
   if (w_dtype < MOE_F32 || w_dtype > MOE_FP4_E2M1) return MOE_ERR_INVALID_ARG;
   if (inter % 64) return MOE_ERR_UNSUPPORTED;
+  if (w_dtype == MOE_FP4_E2M1 &&
+      (inter > F4_MAX_K || !fp4_rows_fit(a_rows, cfg->hidden, rows, inter)))
+    return MOE_ERR_UNSUPPORTED;
   // fp8 and fp4 weights take bf16 activations; fp32 weights take fp32; bf16 takes bf16
   const bool combo = (w_dtype == MOE_F32 && cfg->act_dtype == MOE_F32) ||
                      (w_dtype != MOE_F32 && cfg->act_dtype == MOE_BF16);
