@@ -33,6 +33,15 @@
 #ifndef MOE_RING_WAVES
 #define MOE_RING_WAVES 8
 #endif
+#ifndef MOE_DEC_KERNEL
+#define MOE_DEC_KERNEL 1
+#endif
+#ifndef MOE_DEC_DEPTH
+#define MOE_DEC_DEPTH 2
+#endif
+#ifndef MOE_DEC_KB
+#define MOE_DEC_KB 256
+#endif
 namespace moe {
 
 namespace {
@@ -951,6 +960,140 @@ hipError_t launch_fp4(const GemmArgs& p, GemmShape shape, unsigned grid, hipStre
   return hipErrorInvalidValue;
 }
 
+// --------------------------------------------------------- bf16 decode kernel
+//
+// Decode tiles (16 rows) of bf16 weights, where the launch is a weight
+// stream: gemm_kernel's layout (four waves split N, K through LDS in
+// KB-byte row stages, double buffered) with the loads issued as buffer loads
+// on every path, out-of-range ones (past K, past N, past the group's rows,
+// past the last stage) reading zero without touching memory.  The number of
+// loads in flight is then the same everywhere, the waits are exact, and D
+// stages of loads stay in flight.  Each output element is the same MFMA
+// chain over K, in ascending 32-element steps from zero, as in gemm_kernel,
+// so results do not depend on which kernel computes a tile.
+template <int EPI, int BN, int D, int KB>
+__global__ __launch_bounds__(256) void gemm_dec_kernel(GemmArgs pa) {
+  constexpr int BM = 16;
+  constexpr int ROW = KB + 16;                 // padded LDS row
+  constexpr int CPR = KB / 16;                 // 16-byte chunks per row and stage
+  constexpr int WQ = BN * CPR / 256;           // weight chunks per thread
+  constexpr int AQ = (BM * CPR + 255) / 256;   // activation chunks per thread
+  constexpr int FN = BN / 64;                  // 16-column fragments per wave
+  constexpr int WSZ = BN * ROW;
+  constexpr int STAGE = WSZ + BM * ROW;
+  static_assert(WQ * 256 == BN * CPR, "weight chunks split evenly");
+  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+  Tile t;
+  if (!locate_tile<BM, BN>(pa, t, blockIdx.x)) return;
+  const GemmProblem& p = t.p;
+  const int tid = threadIdx.x;
+  const int wave = tid / WAVE;
+  const int lane = lane_id();
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const uint32_t kbytes = uint32_t(p.k) * 2;
+  const int nst = static_cast<int>((kbytes + KB - 1) / KB);
+
+  // rows of the tile past N lie past the weight buffer's range
+  const int nrows = min(BN, p.n - t.n0);
+  const __amdgpu_buffer_rsrc_t wr =
+      f4_rsrc(static_cast<const char*>(p.w) + (int64_t(t.g) * p.n + t.n0) * kbytes,
+              uint32_t(nrows) * kbytes);
+  uint32_t wbase[WQ], wcol[WQ];
+#pragma unroll
+  for (int q = 0; q < WQ; ++q) {
+    const int c = tid + 256 * q;
+    wbase[q] = uint32_t(c / CPR) * kbytes;
+    wcol[q] = (c % CPR) * 16;
+  }
+  struct Regs {
+    i32x4_t w[WQ], a[AQ];
+  };
+  Regs R[D];
+  auto gload_w = [&](int st, Regs& r) {
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+      const uint32_t k = st * KB + wcol[q];  // past K or past the last stage: zero
+      r.w[q] = __builtin_amdgcn_raw_buffer_load_b128(wr, k < kbytes ? wbase[q] + k : F4_OOB, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) gload_w(d, R[d]);  // the weights do not wait for the rows
+
+  // (the launcher keeps a_rows * K * 2 below 2^31 for this kernel)
+  const int64_t a_all = p.a_rows * int64_t(kbytes);
+  const uint32_t a_range = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(a_all > 0x7fffffff ? 0x7fffffff : a_all));
+  const __amdgpu_buffer_rsrc_t ar = f4_rsrc(p.a, a_range);
+  uint32_t abase[AQ], acol[AQ];
+#pragma unroll
+  for (int q = 0; q < AQ; ++q) {
+    const int c = tid + 256 * q;
+    const int64_t r = t.m0 + c / CPR;
+    acol[q] = (c % CPR) * 16;
+    abase[q] = (c < BM * CPR && r < t.gend) ? static_cast<uint32_t>(src_row(p, r) * kbytes)
+                                              : F4_OOB;
+  }
+  auto gload_a = [&](int st, Regs& r) {
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const uint32_t k = st * KB + acol[q];
+      r.a[q] = __builtin_amdgcn_raw_buffer_load_b128(ar, k < kbytes ? abase[q] + k : F4_OOB, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) gload_a(d, R[d]);
+  auto sstore = [&](int buf, const Regs& r) {
+    char* ws = smem + buf * STAGE;
+    char* as = ws + WSZ;
+#pragma unroll
+    for (int q = 0; q < WQ; ++q) {
+      const int c = tid + 256 * q;
+      *reinterpret_cast<i32x4_t*>(ws + (c / CPR) * ROW + wcol[q]) = r.w[q];
+    }
+#pragma unroll
+    for (int q = 0; q < AQ; ++q) {
+      const int c = tid + 256 * q;
+      if (c < BM * CPR) *reinterpret_cast<i32x4_t*>(as + (c / CPR) * ROW + acol[q]) = r.a[q];
+    }
+  };
+  sstore(0, R[0]);
+  __syncthreads();
+
+  f32x4_t acc[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int st0 = 0; st0 < nst; st0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int st = st0 + d;
+      if (st >= nst) break;
+      // R[d] held stage st (stored last step); it now takes stage st + D
+      gload_w(st + D, R[d]);
+      gload_a(st + D, R[d]);
+      const char* buf = smem + (st & 1) * STAGE;
+      const char* as = buf + WSZ + lrow * ROW + 16 * lgrp;
+      const char* ws = buf + (wave * (BN / 4) + lrow) * ROW + 16 * lgrp;
+#pragma unroll
+      for (int ks = 0; ks < KB / 64; ++ks) {
+        if (st * KB + 64 * ks >= int(kbytes)) break;  // no steps past K
+        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(as + 64 * ks);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const i32x4_t b = *reinterpret_cast<const i32x4_t*>(ws + 16 * j * ROW + 64 * ks);
+          acc[j] = mfma_bf16(a, b, acc[j]);
+        }
+      }
+      if (st + 1 < nst) sstore((st + 1) & 1, R[(d + 1) % D]);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    store_block<K_BF16, EPI>(t, acc[j], t.m0 + 4 * lgrp, t.n0 + wave * (BN / 4) + 16 * j + lrow);
+}
+
 // One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
 // Rows up to QV_MAX * 256 columns are read once into registers (all loads in
 // flight together); longer rows are read twice.
@@ -1037,6 +1180,19 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
   if constexpr (KIND == K_BF16) {
     if (shape.stream && shape.bm == SK_BM && shape.bn == 128)
       return launch_k(gemm_stream_kernel<KIND, 128, EPI>, g, dim3(256), stream, t, p);
+  }
+  if constexpr (KIND == K_BF16) {
+    // decode tiles; its buffer offsets are 32-bit, else gemm_kernel below
+    const bool fits = p.prob[0].a_rows * int64_t(p.prob[0].k) * 2 <= 0x7fffffff &&
+                      p.prob[1].a_rows * int64_t(p.prob[1].k) * 2 <= 0x7fffffff;
+    if (shape.bm == 16 && fits && MOE_DEC_KERNEL) {
+      if (shape.bn == 64)
+        return launch_k(gemm_dec_kernel<EPI, 64, MOE_DEC_DEPTH, MOE_DEC_KB>, g, dim3(256), stream,
+                        t, p);
+      if (shape.bn == 128)
+        return launch_k(gemm_dec_kernel<EPI, 128, MOE_DEC_DEPTH, MOE_DEC_KB>, g, dim3(256),
+                        stream, t, p);
+    }
   }
   if (shape.bm == 16 && shape.bn == 64)
     return launch_k(gemm_kernel<KIND, 16, 64, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
