@@ -15,14 +15,21 @@
 // per-expert counts.  A rows are gathered through the routing permutation
 // while loading, so the permuted activations never exist in memory.
 //
-// K is streamed in 128-byte stages through a double buffer in LDS (rows
-// padded to 144 bytes against bank conflicts), the next stage's global loads
-// issued before the current stage's MFMAs.  Tile shapes: 16 x 128 for decode
-// (an expert sees a handful of tokens: each weight byte feeds one MFMA and
-// the launch is a weight stream), 64 x 128 and 128 x 128 for prefill.
+// Kernels, by tile shape (pick_gemm_shape):
+//  * decode, a handful of rows per expert (each weight byte feeds one MFMA:
+//    the launch is a weight stream): 16 x 64 tiles, gemm_dec_kernel for bf16
+//    weights (buffer loads, two stages in flight), gemm_kernel otherwise;
+//  * 64 x 128 and 128 x 128 tiles: gemm_kernel, K in 128-byte stages through
+//    a double buffer in LDS, the next stage's loads issued before the current
+//    stage's MFMAs;
+//  * hundreds of rows per expert: 256 x 256 tiles, gemm_ring_kernel (K in
+//    64-byte slices fetched straight into a 4-stage LDS ring);
+//  * the router's logits (a dense GEMM against the small gate matrix):
+//    gemm_stream_kernel, thin tiles over a DMA ring;
+//  * MXFP4 weights: gemm_fp4_kernel (16- or 64-row tiles).
 // Every output element accumulates its K steps in ascending order with the
-// same MFMA, whichever tile shape computes it, so results do not depend on
-// the launch configuration.
+// same MFMA, whichever tile shape computes it (for fp4: the same order for
+// both of its shapes), so results do not depend on the launch configuration.
 #include <type_traits>
 
 #include "internal.hpp"
@@ -1189,15 +1196,10 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
       if (shape.bn == 64)
         return launch_k(gemm_dec_kernel<EPI, 64, MOE_DEC_DEPTH, MOE_DEC_KB>, g, dim3(256), stream,
                         t, p);
-      if (shape.bn == 128)
-        return launch_k(gemm_dec_kernel<EPI, 128, MOE_DEC_DEPTH, MOE_DEC_KB>, g, dim3(256),
-                        stream, t, p);
     }
   }
   if (shape.bm == 16 && shape.bn == 64)
     return launch_k(gemm_kernel<KIND, 16, 64, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
-  if (shape.bm == 16)
-    return launch_k(gemm_kernel<KIND, 16, 128, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if (shape.bm == 64)
     return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if constexpr (KIND == K_BF16) {
@@ -1226,13 +1228,13 @@ hipError_t launch_kind(const GemmArgs& p, int epi, GemmShape shape, unsigned gri
 
 }  // namespace
 
-GemmShape pick_gemm_shape(int kind, int64_t rows, int groups, bool down) {
+GemmShape pick_gemm_shape(int kind, int64_t rows, int groups) {
   const int64_t avg = groups > 0 ? rows / groups : rows;
   // 4-bit weights: a weight stream for decode; wider M tiles re-read it less
   if (kind == K_FP4) return GemmShape{avg <= 24 ? 16 : 64, 64};
-  // decode: a weight stream; the up projection (K = hidden) streams best in
-  // 64-wide tiles, the down projection (K = inter) in 128-wide ones
-  if (avg <= 24) return GemmShape{16, down ? 128 : 64};
+  // decode: a weight stream, in 16 x 64 tiles (more tiles in flight than
+  // 128-wide ones)
+  if (avg <= 24) return GemmShape{16, 64};
   if (avg <= 80) return GemmShape{64, 128};
   if (avg < 128 || kind == K_F32) return GemmShape{128, 128};
   return GemmShape{256, 256};

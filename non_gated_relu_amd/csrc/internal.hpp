@@ -169,9 +169,9 @@ hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t strea
 hipError_t launch_quant(const QuantArgs& p, hipStream_t stream, Timing t = {});
 
 // Pick the tile shape for a grouped GEMM with `rows` problem rows over
-// `groups` matrices (the up or the down projection of an MLP; both use the
-// same BM, so they share one M-tile schedule).
-GemmShape pick_gemm_shape(int kind, int64_t rows, int groups, bool down);
+// `groups` matrices (the up and the down projection of an MLP use the same
+// shape, so they share one M-tile schedule).
+GemmShape pick_gemm_shape(int kind, int64_t rows, int groups);
 // Upper bound of the M tiles a schedule of this shape can hold.
 int64_t max_mtiles(int64_t rows, int groups, int bm);
 // Launch one grouped GEMM (schedule already built for shape.bm).

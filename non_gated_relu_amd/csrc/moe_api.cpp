@@ -138,15 +138,13 @@ struct Mlp {
 // Shape and tile bound of a launch over `main` (+ `extra_rows` of a second
 // single-group problem).
 struct FfnPlan {
-  GemmShape shape;       // up projection
-  GemmShape down_shape;  // down projection (same BM)
+  GemmShape shape;  // both projections
   int64_t mtiles;
 };
 
 FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats, int64_t extra_rows) {
   FfnPlan f;
-  f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats, false);
-  f.down_shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats, true);
+  f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats);
   f.mtiles = max_mtiles(rows, n_mats, f.shape.bm) +
              (extra_rows > 0 ? (extra_rows + f.shape.bm - 1) / f.shape.bm : 0);
   return f;
@@ -241,8 +239,8 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   if (extra) dn.prob[1] = down_problem(*extra, hidden);
   dn.sched = sched;
   dn.n_groups = m.n_mats;
-  dn.n_tiles = (hidden + f.down_shape.bn - 1) / f.down_shape.bn;
-  if (launch_gemm(dn, kind, EPI_PLAIN, f.down_shape, f.mtiles, s, tm.down) != hipSuccess)
+  dn.n_tiles = (hidden + f.shape.bn - 1) / f.shape.bn;
+  if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
