@@ -65,6 +65,7 @@ class Workload:
     bias_boost_value: float = 0.0
     seed: int = 0
     shared_dtype: str = None  # shared-expert weights; None = act_dtype
+    norm_eps: float = 1e-5    # the block's RMSNorm eps (layer_norm_epsilon)
 
     @property
     def shared_weight_dtype(self) -> str:
@@ -192,7 +193,9 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     likewise ws_up_bscale [Is,d/32] and ws_down_bscale [d,Is/32] with packed
     ws_up [Is,d/2] and ws_down [d,Is/2] when the shared expert is fp4.
     bf16 tensors are uint16 bit patterns, fp8 / fp4 tensors uint8 codes.
-    ``experts=False`` skips the routed expert weights (router-only work).
+    norm_w [d] (act dtype) is the weight of the RMSNorm before the layer in
+    its block.  ``experts=False`` skips the routed expert weights (router-only
+    work).
     """
     T, d, E, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.inter, wl.shared_inter
     root = np.random.SeedSequence(wl.seed)
@@ -205,6 +208,10 @@ def make_inputs(wl: Workload, experts: bool = True, threads: int = 8) -> dict:
     for e in wl.bias_boost:
         b[e] = b[e] + np.float32(wl.bias_boost_value)
     out["e_bias"] = b.astype(np.float32)
+    # the block's RMSNorm weight, 1 + N(0, 0.1), from a stream of its own
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, 8])))
+    out["norm_w"] = _store(np.float32(1.0) + g.standard_normal(d, dtype=np.float32)
+                           * np.float32(0.1), wl.act_dtype)
     out["w_up_scale"] = out["w_down_scale"] = None
     out["w_up_bscale"] = out["w_down_bscale"] = None
     out["ws_up_bscale"] = out["ws_down_bscale"] = None

@@ -131,6 +131,37 @@ def quantize_rows(v):
 
 # ----------------------------------------------------------------- router
 
+def rmsnorm(x, g, eps: float, dtype: str) -> np.ndarray:
+    """The block's pre-mixer RMSNorm of rows x [T, d] with weight g [d], in the
+    precision the C oracle states; returns storage form (fp32, or bf16 bits)."""
+    x = _c(x)
+    g = _c(g)
+    T, d = x.shape
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), ctypes.c_int(_DT[dtype]), _p(g), ctypes.c_float(eps),
+                      ctypes.c_int64(T), ctypes.c_int64(d), _p(out))
+    return out
+
+
+def block_forward(wl, inp: dict, tokens=None, mode: int = AS_CONFIGURED):
+    """block(x) = x + MoE(RMSNorm(x)) for the listed tokens, fp64 (the
+    residual add is exact here; the layer runs on the rounded x_norm).
+
+    Returns forward()'s dict with y replaced by the block output, plus x_norm
+    (storage form, all tokens)."""
+    xn = rmsnorm(inp["x"], inp["norm_w"], wl.norm_eps, wl.act_dtype)
+    out = forward(wl, dict(inp, x=xn), tokens=tokens, mode=mode)
+    x = inp["x"] if wl.act_dtype == "f32" else _bf16_bits_to_f64(inp["x"])
+    out["y"] = np.asarray(x, np.float64)[out["tokens"]] + out["y"]
+    out["x_norm"] = xn
+    return out
+
+
+def _bf16_bits_to_f64(b) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def route(wl, x, w_gate, e_bias, logits=False):
     """Grouped top-k routing of every row of x.
 

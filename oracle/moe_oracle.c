@@ -93,7 +93,7 @@ typedef struct {
 #include <omp.h>
 #endif
 
-int orc_version(void) { return 5; }
+int orc_version(void) { return 6; }
 
 /* Threads an OpenMP loop of the oracle uses. */
 int orc_num_threads(void) {
@@ -284,6 +284,51 @@ static double dot_row(const double* a, orc_mat m, int64_t row, int64_t n) {
     }
   }
   return acc;
+}
+
+/* ------------------------------------------------------------ block norm */
+
+/* The block around the layer (exo commit "Add support for Nemotron sharding":
+ * the NemotronHBlock stub holds a pre-mixer RMSNorm and the mixer; the MLX
+ * RMSNorm stub: a weight over the feature dimension and an additive eps):
+ *   block(x) = x + MoE(RMSNorm(x)),   RMSNorm(x)_i = x_i / sqrt(mean_i(x^2) + eps) * g_i
+ * The norm's output takes the type of its weight, the layer's activation type
+ * (auto-round PR, discussion of norm_dtype).  Precision (this library's
+ * reading, fixed so that every implementation rounds x_norm the same way):
+ * the sum of squares in fp64 (exact, so its order does not matter, while the
+ * squares lie within a factor 2^37 of each other: a bf16 square has 16
+ * significant bits, fp64 keeps 53); var = fp32(ss / d);
+ * r = 1 / sqrt(var + eps) in fp32; n_i = (x_i * r) * g_i in fp32, rounded
+ * once to the storage type (nearest even).  Rows [T, d] of dtype dt (fp32 or
+ * bf16 bits); g [d] of the same dtype. */
+void orc_rmsnorm(const void* x, int dt, const void* g, float eps, int64_t T, int64_t d,
+                 void* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < d; ++i) {
+      double v = dt == ORC_F32 ? (double)((const float*)x)[t * d + i]
+                               : orc_bf16_to_double(((const uint16_t*)x)[t * d + i]);
+      ss += v * v;
+    }
+    float var = (float)(ss / (double)d);
+    float r = 1.0f / sqrtf(var + eps);
+    for (int64_t i = 0; i < d; ++i) {
+      float xi, gi;
+      if (dt == ORC_F32) {
+        xi = ((const float*)x)[t * d + i];
+        gi = ((const float*)g)[i];
+      } else {
+        xi = (float)orc_bf16_to_double(((const uint16_t*)x)[t * d + i]);
+        gi = (float)orc_bf16_to_double(((const uint16_t*)g)[i]);
+      }
+      float n = (xi * r) * gi;
+      if (dt == ORC_F32)
+        ((float*)out)[t * d + i] = n;
+      else
+        ((uint16_t*)out)[t * d + i] = orc_bf16_from_double((double)n);
+    }
+  }
 }
 
 /* ---------------------------------------------------------------- router */
