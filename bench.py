@@ -2,7 +2,8 @@
 
 One step = one ``moe_forward`` call (route -> permute -> routed expert MLPs ->
 shared expert -> combine) over one batch of seeded synthetic tokens that are
-already resident in HBM.  Prints one JSON line.
+already resident in HBM; for the block workloads one ``moe_block_forward``
+(RMSNorm first, the residual added in combine).  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
@@ -30,7 +31,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "decode-bf16-T32"
 DEFAULT_STEPS = {"tiny-f32-T64": 200, "decode-bf16-T32": 200, "prefill-bf16-T4096": 50,
-                 "skew-bf16-T16384": 20, "fp8-T8192": 30, "decode-fp4-T32": 200}
+                 "skew-bf16-T16384": 20, "fp8-T8192": 30, "decode-fp4-T32": 200,
+                 "block-decode-bf16-T32": 200}
 # kernels whose counter readings are reported as "traffic"
 TRAFFIC_SOURCES = ["non_gated_relu_amd/csrc/gemm.hip", "non_gated_relu_amd/csrc/common.hpp",
                    "non_gated_relu_amd/csrc/internal.hpp"]
@@ -96,6 +98,10 @@ def stage_work(wl, active: int):
             w["shared_down"] = dict(sh_dn, dtype=mfma_dtype(sdt), unit_bytes=sd, units=1)
     w["combine"] = dict(bytes=S * d * 4 + T * d * 4 * (1 if Is else 0) + T * d * ae + S * 8,
                         flops=0, dtype="f32")
+    if getattr(wl, "block", False):
+        # the norm reads x and writes x_norm; combine also reads the residual x
+        w["norm"] = dict(bytes=2 * T * d * ae + d * ae, flops=0, dtype="f32")
+        w["combine"]["bytes"] += T * d * ae
     return w
 
 
@@ -107,6 +113,8 @@ def layer_work(wl, active: int):
     flops = T * (2 * d * E + k * 4 * d * I + 4 * d * Is)
     byts = (active * (wbytes(edt, I, d) + wbytes(edt, d, I)) + wbytes(sdt, Is, d) +
             wbytes(sdt, d, Is) + E * d * ae + E * 4 + 2 * T * d * ae)
+    if getattr(wl, "block", False):
+        byts += d * ae  # the norm weight (x is read once and y written once either way)
     return flops, byts
 
 
@@ -143,7 +151,8 @@ def cpu_baseline(wl, inp, y_gpu, idx_gpu, budget_s: float):
     reps, elapsed, out = 0, 0.0, None
     t0 = time.perf_counter()
     while reps == 0 or (elapsed < budget_s and reps < 1000):
-        out = oracle.forward(wl, inp, tokens=tokens)
+        out = (oracle.block_forward(wl, inp, tokens=tokens) if getattr(wl, "block", False)
+               else oracle.forward(wl, inp, tokens=tokens))
         reps += 1
         elapsed = time.perf_counter() - t0
     R = float(np.sqrt(np.mean(out["y"] ** 2)))
@@ -204,18 +213,25 @@ def main():
     layer = binding.MoELayer(wl, inp, device=dev)
     x = binding.to_device(inp["x"], dev, "x", wl)
     y = torch.empty((wl.tokens, wl.hidden), dtype=x.dtype, device=dev)
-    stages = binding.stages_of(wl)
+    block = bool(getattr(wl, "block", False))
+    stages = binding.stages_of(wl, block=block)
+
+    def run(ev):
+        if block:
+            layer.block(x, out=y, stage_events=ev)
+        else:
+            layer(x, y=y, stage_events=ev)
     # one set of kernel timestamp events per timed step, read after the region
     evs = [binding.StageEvents() for _ in range(steps)]
 
     print(f"bench: warmup {args.warmup}, timing {steps} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        layer(x, y=y, stage_events=evs[i % steps])
+        run(evs[i % steps])
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     for i in range(steps):
-        layer(x, y=y, stage_events=evs[i])
+        run(evs[i])
     torch.cuda.synchronize()
     total_s = time.perf_counter() - t0
 
@@ -229,7 +245,7 @@ def main():
     # the same step replayed from a HIP graph: no per-kernel launch gaps
     graph_s = None
     if not args.no_graph:
-        gstep = binding.GraphStep(layer, x, y)
+        gstep = binding.GraphStep(layer, x, y, block=block)
         for _ in range(args.warmup):
             gstep.replay()
         torch.cuda.synchronize()
@@ -287,7 +303,8 @@ def main():
                        "topk_group": wl.topk_group, "top_k": wl.top_k, "inter": wl.inter,
                        "shared_inter": wl.shared_inter, "expert_dtype": wl.expert_dtype,
                        "parallelism": "single GPU"},
-            "launch": "hipGraph replay of moe_forward" if graph_s else "eager moe_forward",
+            "launch": ("hipGraph replay of " if graph_s else "eager ") +
+                      ("moe_block_forward" if block else "moe_forward"),
             "eager_ms_per_step": 1e3 * eager_s / steps,
             "roofline": roofline, "layer": layer_fig,
             "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}

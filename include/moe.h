@@ -216,7 +216,8 @@ enum {
   MOE_T_SHARED_UP = 6,    /* shared-expert up GEMM + relu^2               */
   MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM                      */
   MOE_T_COMBINE = 8,      /* weighted combine + output rounding           */
-  MOE_T_SLOTS = 9
+  MOE_T_NORM = 9,         /* block only: the RMSNorm before the layer     */
+  MOE_T_SLOTS = 10
 };
 moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
                              const void* w_gate, const float* e_bias, const void* w_up,
@@ -227,6 +228,53 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
                              float* topk_w, int32_t* expert_counts,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* const* stage_events);
+
+/* ------------------------------------------------------------------------
+ * The block around the layer (exo commit "Add support for Nemotron
+ * sharding": the NemotronHBlock stub holds a pre-mixer RMSNorm and the
+ * mixer; the MLX RMSNorm stub: a weight and an additive eps):
+ *     out = x + MoE(RMSNorm(x)),   RMSNorm(x)_i = x_i / sqrt(mean(x^2) + eps) * g_i
+ * The norm's output is held in act_dtype, its weight's type (auto-round PR,
+ * discussion of norm_dtype).  Precision of the norm: sum of squares in fp64;
+ * var = fp32(ss / d); r = 1 / sqrt(var + eps) in fp32 (correctly rounded);
+ * n_i = (x_i * r) * g_i in fp32, rounded once (nearest even) to act_dtype.
+ * For bf16 rows (squares within a factor 2^37 of each other) the fp64 sum
+ * is exact, so the normalised rows are the same bits in any implementation
+ * of this rule.
+ */
+
+/* RMSNorm of rows: x [tokens, d], weight [d], out [tokens, d], all act_dtype.
+ * eps finite and >= 0.  out may not alias x. */
+moe_status moe_rmsnorm(const moe_config* cfg, int64_t tokens, const void* x, const void* weight,
+                       float eps, void* out, void* stream);
+
+/* Bytes of workspace moe_block_forward needs (host output): moe_forward's
+ * plus the normalised rows. */
+moe_status moe_block_workspace_size(const moe_config* cfg, int64_t tokens, size_t* bytes);
+
+/* The block: out = x + MoE(RMSNorm(x)).  Arguments as moe_forward, plus the
+ * norm's weight [d] act_dtype and eps.  The layer routes and runs on the
+ * normalised rows; the combine adds the residual x to the fp32 sum before its
+ * one rounding.  out may alias x (an in-place residual update).  Stage
+ * events as moe_forward_timed, with MOE_T_NORM for the norm. */
+moe_status moe_block_forward(const moe_config* cfg, int64_t tokens, const void* x,
+                             const void* norm_weight, float eps, const void* w_gate,
+                             const float* e_bias, const void* w_up, const void* w_up_scale,
+                             const void* w_down, const void* w_down_scale, const void* ws_up,
+                             const void* ws_up_scale, const void* ws_down,
+                             const void* ws_down_scale, void* out, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts, void* workspace,
+                             size_t workspace_bytes, void* stream);
+moe_status moe_block_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
+                                   const void* norm_weight, float eps, const void* w_gate,
+                                   const float* e_bias, const void* w_up,
+                                   const void* w_up_scale, const void* w_down,
+                                   const void* w_down_scale, const void* ws_up,
+                                   const void* ws_up_scale, const void* ws_down,
+                                   const void* ws_down_scale, void* out, int32_t* topk_idx,
+                                   float* topk_w, int32_t* expert_counts, void* workspace,
+                                   size_t workspace_bytes, void* stream,
+                                   void* const* stage_events);
 
 /* Static text for a status code. */
 const char* moe_status_string(moe_status status);

@@ -70,9 +70,16 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [_vp]
+        L.moe_rmsnorm.argtypes = [_cfgp, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]
+        L.moe_block_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_block_forward.argtypes = ([_cfgp, _i64, _vp, _vp, ctypes.c_float] +
+                                        [_vp] * 15 + [ctypes.c_size_t, _vp])
+        L.moe_block_forward_timed.argtypes = L.moe_block_forward.argtypes + [_vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
-                     "moe_forward", "moe_forward_timed"):
+                     "moe_forward", "moe_forward_timed", "moe_rmsnorm",
+                     "moe_block_workspace_size", "moe_block_forward",
+                     "moe_block_forward_timed"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -204,7 +211,7 @@ def combine(cfg: MoeConfig, slot_pos, topk_w, y_perm, shared_out=None, y=None):
 
 
 STAGES = ("route", "permute", "quant_x", "routed_up", "quant_h", "routed_down", "shared_up",
-          "shared_down", "combine")
+          "shared_down", "combine", "norm")
 
 
 def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_up_scale=None,
@@ -230,6 +237,43 @@ def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_u
     return y
 
 
+def block_workspace_size(cfg: MoeConfig, tokens: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().moe_block_workspace_size(ctypes.byref(cfg), tokens, ctypes.byref(n)),
+           "moe_block_workspace_size")
+    return n.value
+
+
+def rmsnorm(cfg: MoeConfig, x, weight, eps: float, out=None):
+    """The block's RMSNorm of rows x (see moe.h)."""
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().moe_rmsnorm(ctypes.byref(cfg), x.shape[0], _p(x), _p(weight), float(eps),
+                             _p(out), _stream()), "moe_rmsnorm")
+    return out
+
+
+def block_forward(cfg: MoeConfig, x, norm_weight, eps: float, w_gate, e_bias, w_up, w_down,
+                  ws_up, ws_down, w_up_scale=None, w_down_scale=None, ws_up_scale=None,
+                  ws_down_scale=None, ws=None, out=None, topk_idx=None, topk_w=None,
+                  expert_counts=None, stage_events=None):
+    """out = x + MoE(RMSNorm(x)): moe_block_forward (moe_block_forward_timed with
+    ``stage_events``).  ``out`` may be ``x`` itself."""
+    T = x.shape[0]
+    out = torch.empty_like(x) if out is None else out
+    if ws is None:
+        ws = workspace(block_workspace_size(cfg, T), x)
+    args = [ctypes.byref(cfg), T, _p(x), _p(norm_weight), float(eps), _p(w_gate), _p(e_bias),
+            _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(ws_up), _p(ws_up_scale),
+            _p(ws_down), _p(ws_down_scale), _p(out), _p(topk_idx), _p(topk_w),
+            _p(expert_counts), _p(ws), ws.numel(), _stream()]
+    if stage_events is None:
+        _check(lib().moe_block_forward(*args), "moe_block_forward")
+    else:
+        _check(lib().moe_block_forward_timed(*args, stage_events.array),
+               "moe_block_forward_timed")
+    return out
+
+
 class StageEvents:
     """One start/stop event pair per stage of moe_forward_timed."""
 
@@ -246,10 +290,11 @@ class StageEvents:
             self.events[2 * STAGES.index(s) + 1]) for s in stages}
 
 
-def stages_of(wl):
-    """The stages moe_forward runs for a workload (the shared expert has launches
-    of its own only when its weight type differs from the routed experts')."""
-    st = ["route", "permute"]
+def stages_of(wl, block: bool = False):
+    """The stages moe_forward (or, with ``block``, moe_block_forward) runs for a
+    workload (the shared expert has launches of its own only when its weight
+    type differs from the routed experts')."""
+    st = (["norm"] if block else []) + ["route", "permute"]
     if wl.expert_dtype == "fp8":
         st += ["quant_x", "routed_up", "quant_h", "routed_down"]
     else:
@@ -273,8 +318,9 @@ class MoELayer:
         self.t = {k: to_device(v, device, k, wl) for k, v in tensors.items()
                   if v is not None and k != "x"}
         self.max_tokens = max_tokens or wl.tokens
-        self.ws = torch.empty(workspace_size(self.cfg, self.max_tokens), dtype=torch.uint8,
-                              device=self.device)
+        # (the block's workspace holds the layer's and the normalised rows)
+        self.ws = torch.empty(block_workspace_size(self.cfg, self.max_tokens),
+                              dtype=torch.uint8, device=self.device)
         T, k = self.max_tokens, wl.top_k
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=self.device)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=self.device)
@@ -294,6 +340,21 @@ class MoELayer:
                        ws_up_scale=t.get("ws_up_bscale"), ws_down_scale=t.get("ws_down_bscale"))
 
 
+    def block(self, x, out=None, stage_events=None):
+        """out = x + layer(RMSNorm(x)) (moe_block_forward); ``out`` may be ``x``."""
+        T = x.shape[0]
+        if T > self.max_tokens:
+            raise ValueError(f"{T} tokens exceed the workspace sized for {self.max_tokens}")
+        t = self.t
+        return block_forward(self.cfg, x, t["norm_w"], self.wl.norm_eps, t["w_gate"],
+                             t["e_bias"], t["w_up"], t["w_down"], t.get("ws_up"),
+                             t.get("ws_down"), t.get("w_up_scale", t.get("w_up_bscale")),
+                             t.get("w_down_scale", t.get("w_down_bscale")),
+                             t.get("ws_up_bscale"), t.get("ws_down_bscale"), ws=self.ws, out=out,
+                             topk_idx=self.topk_idx[:T], topk_w=self.topk_w[:T],
+                             expert_counts=self.expert_counts, stage_events=stage_events)
+
+
 class GraphStep:
     """One MoELayer forward captured in a HIP graph (torch.cuda.CUDAGraph).
 
@@ -302,16 +363,23 @@ class GraphStep:
     current contents of ``x``.
     """
 
-    def __init__(self, layer: MoELayer, x, y):
+    def __init__(self, layer: MoELayer, x, y, block: bool = False):
         self.x, self.y = x, y
+
+        def step():
+            if block:  # the block around the layer: y = x + layer(RMSNorm(x))
+                layer.block(x, out=y)
+            else:
+                layer(x, y=y)
+
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            layer(x, y=y)
+            step()
         torch.cuda.current_stream().wait_stream(side)
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
-            layer(x, y=y)
+            step()
 
     def replay(self):
         self.graph.replay()

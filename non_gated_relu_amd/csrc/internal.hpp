@@ -100,9 +100,19 @@ struct CombineArgs {
   const float* topk_w;
   const float* y_perm;
   const float* shared;
+  const void* residual;  // [tokens, hidden] in the output type, or null
   void* y;
   int64_t tokens;
   int hidden, top_k;
+};
+
+struct NormArgs {
+  const void* x;       // [tokens, hidden] activation type
+  const void* weight;  // [hidden] activation type
+  void* out;           // [tokens, hidden] activation type
+  int64_t tokens;
+  int hidden;
+  float eps;
 };
 
 enum Epilogue : int { EPI_RELU2 = 0, EPI_PLAIN = 1 };
@@ -167,6 +177,7 @@ hipError_t launch_gather(const GatherArgs& p, hipStream_t stream);
 hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t = {});
 hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream, Timing t = {});
 hipError_t launch_quant(const QuantArgs& p, hipStream_t stream, Timing t = {});
+hipError_t launch_rmsnorm(const NormArgs& p, bool bf16, hipStream_t stream, Timing t = {});
 
 // Pick the tile shape for a grouped GEMM with `rows` problem rows over
 // `groups` matrices (the up and the down projection of an MLP use the same

@@ -362,11 +362,104 @@ size_t carve_standalone(Carver& cv, Mlp& m, int hidden, int32_t** sched) {
   return cv.used;
 }
 
+struct LayerWeights {
+  const void* w_gate;
+  const float* e_bias;
+  const void *w_up, *w_up_scale, *w_down, *w_down_scale;
+  const void *ws_up, *ws_up_scale, *ws_down, *ws_down_scale;
+};
+
+// Bytes of the block's normalised rows in the workspace.
+size_t norm_bytes(const moe_config& c, int64_t T) { return size_t(T) * c.hidden * esize(c.act_dtype); }
+
+// The layer on x (norm_weight null), or the block x + layer(RMSNorm(x)): the
+// norm's rows go to the workspace after the layer's own part, the layer runs
+// on them, and the combine adds x before its rounding.
+moe_status run_forward(const moe_config* cfg, int64_t tokens, const void* x,
+                       const void* norm_weight, float eps, const LayerWeights& w, void* y,
+                       int32_t* topk_idx, float* topk_w, int32_t* expert_counts, void* workspace,
+                       size_t workspace_bytes, void* stream, void* const* ev) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
+  if (tokens == 0) return MOE_OK;
+  const moe_config& c = *cfg;
+  const bool block = norm_weight != nullptr;
+  const void* ptrs[] = {x, w.w_gate, w.e_bias, w.w_up, w.w_down, y};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  if (c.shared_inter > 0 &&
+      (!w.ws_up || !w.ws_down || !aligned16(w.ws_up) || !aligned16(w.ws_down)))
+    return MOE_ERR_INVALID_ARG;
+  if ((c.expert_dtype == MOE_FP8_E4M3 || c.expert_dtype == MOE_FP4_E2M1) &&
+      (!w.w_up_scale || !w.w_down_scale || !aligned16(w.w_up_scale) ||
+       !aligned16(w.w_down_scale)))
+    return MOE_ERR_INVALID_ARG;
+  if (c.shared_inter > 0 && c.shared_dtype == MOE_FP4_E2M1 &&
+      (!w.ws_up_scale || !w.ws_down_scale || !aligned16(w.ws_up_scale) ||
+       !aligned16(w.ws_down_scale)))
+    return MOE_ERR_INVALID_ARG;
+  const void* outs[] = {topk_idx, topk_w, expert_counts};
+  for (const void* p : outs)
+    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  Carver measure(nullptr);
+  carve_forward(measure, c, tokens);
+  if (block) measure.take<char>(norm_bytes(c, tokens));
+  if (!workspace || workspace_bytes < measure.used || !aligned16(workspace))
+    return MOE_ERR_WORKSPACE;
+  Carver cv(workspace);
+  Forward f = carve_forward(cv, c, tokens);
+  void* xn = block ? cv.take<char>(norm_bytes(c, tokens)) : nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
+  float* wts = topk_w ? topk_w : f.topk_w;
+  int32_t* cnt = expert_counts ? expert_counts : f.counts;
+  if (block) {
+    NormArgs na{x, norm_weight, xn, tokens, c.hidden, eps};
+    if (launch_rmsnorm(na, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_NORM)) != hipSuccess)
+      return MOE_ERR_HIP;
+  }
+  const void* xl = block ? xn : x;  // the layer's input rows
+  f.routed.a = xl;
+  f.routed.w_up = w.w_up;
+  f.routed.up_scale = w.w_up_scale;
+  f.routed.w_down = w.w_down;
+  f.routed.down_scale = w.w_down_scale;
+  f.shared.a = xl;
+  f.shared.w_up = w.ws_up;
+  f.shared.up_scale = c.shared_dtype == MOE_FP4_E2M1 ? w.ws_up_scale : nullptr;
+  f.shared.w_down = w.ws_down;
+  f.shared.down_scale = c.shared_dtype == MOE_FP4_E2M1 ? w.ws_down_scale : nullptr;
+
+  const RouteArgs ra = route_args(c, tokens, xl, w.w_gate, w.e_bias, idx, wts, f.logits);
+  if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  const ScheduleSpec spec{f.sched, f.fused_shared ? tokens : 0, f.plan.shape.bm,
+                          static_cast<int>(f.plan.mtiles)};
+  if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
+                       f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
+    return st;
+  FfnTiming rt{slot(ev, MOE_T_QUANT_X), slot(ev, MOE_T_ROUTED_UP), slot(ev, MOE_T_QUANT_H),
+               slot(ev, MOE_T_ROUTED_DOWN)};
+  if ((st = run_mlps(c.hidden, f.routed, f.fused_shared ? &f.shared : nullptr, f.sched, true, s,
+                     rt)) != MOE_OK)
+    return st;
+  if (c.shared_inter > 0 && !f.fused_shared) {
+    FfnTiming sh{Timing{}, slot(ev, MOE_T_SHARED_UP), Timing{}, slot(ev, MOE_T_SHARED_DOWN)};
+    if ((st = run_mlps(c.hidden, f.shared, nullptr, f.shared_sched, false, s, sh)) != MOE_OK)
+      return st;
+  }
+  CombineArgs p{f.slot_pos, wts, f.routed.out, c.shared_inter > 0 ? f.shared.out : nullptr,
+                block ? x : nullptr, y, tokens, c.hidden, c.top_k};
+  return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_COMBINE)));
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 2; }
+int32_t moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(moe_status st) {
   switch (st) {
@@ -514,7 +607,8 @@ moe_status moe_combine(const moe_config* cfg, int64_t tokens, const int32_t* slo
   for (const void* p : ptrs)
     if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
   if (shared_out && !aligned16(shared_out)) return MOE_ERR_INVALID_ARG;
-  CombineArgs p{slot_pos, topk_w, y_perm, shared_out, y, tokens, cfg->hidden, cfg->top_k};
+  CombineArgs p{slot_pos, topk_w, y_perm, shared_out, nullptr, y, tokens, cfg->hidden,
+                cfg->top_k};
   return hip_status(launch_combine(p, cfg->act_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
 }
 
@@ -527,68 +621,10 @@ moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* 
                              float* topk_w, int32_t* expert_counts,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* const* ev) {
-  moe_status st = check_config(cfg);
-  if (st != MOE_OK) return st;
-  if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
-  if (tokens == 0) return MOE_OK;
-  const moe_config& c = *cfg;
-  const void* ptrs[] = {x, w_gate, e_bias, w_up, w_down, y};
-  for (const void* p : ptrs)
-    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
-  if (c.shared_inter > 0 && (!ws_up || !ws_down || !aligned16(ws_up) || !aligned16(ws_down)))
-    return MOE_ERR_INVALID_ARG;
-  if ((c.expert_dtype == MOE_FP8_E4M3 || c.expert_dtype == MOE_FP4_E2M1) &&
-      (!w_up_scale || !w_down_scale || !aligned16(w_up_scale) || !aligned16(w_down_scale)))
-    return MOE_ERR_INVALID_ARG;
-  if (c.shared_inter > 0 && c.shared_dtype == MOE_FP4_E2M1 &&
-      (!ws_up_scale || !ws_down_scale || !aligned16(ws_up_scale) || !aligned16(ws_down_scale)))
-    return MOE_ERR_INVALID_ARG;
-  const void* outs[] = {topk_idx, topk_w, expert_counts};
-  for (const void* p : outs)
-    if (p && !aligned16(p)) return MOE_ERR_INVALID_ARG;
-  Carver measure(nullptr);
-  carve_forward(measure, c, tokens);
-  if (!workspace || workspace_bytes < measure.used || !aligned16(workspace))
-    return MOE_ERR_WORKSPACE;
-  Carver cv(workspace);
-  Forward f = carve_forward(cv, c, tokens);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t* idx = topk_idx ? topk_idx : f.topk_idx;
-  float* wts = topk_w ? topk_w : f.topk_w;
-  int32_t* cnt = expert_counts ? expert_counts : f.counts;
-  f.routed.a = x;
-  f.routed.w_up = w_up;
-  f.routed.up_scale = w_up_scale;
-  f.routed.w_down = w_down;
-  f.routed.down_scale = w_down_scale;
-  f.shared.a = x;
-  f.shared.w_up = ws_up;
-  f.shared.up_scale = c.shared_dtype == MOE_FP4_E2M1 ? ws_up_scale : nullptr;
-  f.shared.w_down = ws_down;
-  f.shared.down_scale = c.shared_dtype == MOE_FP4_E2M1 ? ws_down_scale : nullptr;
-
-  const RouteArgs ra = route_args(c, tokens, x, w_gate, e_bias, idx, wts, f.logits);
-  if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  const ScheduleSpec spec{f.sched, f.fused_shared ? tokens : 0, f.plan.shape.bm,
-                          static_cast<int>(f.plan.mtiles)};
-  if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
-                       f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
-    return st;
-  FfnTiming rt{slot(ev, MOE_T_QUANT_X), slot(ev, MOE_T_ROUTED_UP), slot(ev, MOE_T_QUANT_H),
-               slot(ev, MOE_T_ROUTED_DOWN)};
-  if ((st = run_mlps(c.hidden, f.routed, f.fused_shared ? &f.shared : nullptr, f.sched, true, s,
-                     rt)) != MOE_OK)
-    return st;
-  if (c.shared_inter > 0 && !f.fused_shared) {
-    FfnTiming sh{Timing{}, slot(ev, MOE_T_SHARED_UP), Timing{}, slot(ev, MOE_T_SHARED_DOWN)};
-    if ((st = run_mlps(c.hidden, f.shared, nullptr, f.shared_sched, false, s, sh)) != MOE_OK)
-      return st;
-  }
-  CombineArgs p{f.slot_pos, wts, f.routed.out, c.shared_inter > 0 ? f.shared.out : nullptr, y,
-                tokens, c.hidden, c.top_k};
-  return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_COMBINE)));
+  const LayerWeights w{w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
+                       ws_up, ws_up_scale, ws_down, ws_down_scale};
+  return run_forward(cfg, tokens, x, nullptr, 0.0f, w, y, topk_idx, topk_w, expert_counts,
+                     workspace, workspace_bytes, stream, ev);
 }
 
 moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, const void* w_gate,
@@ -600,6 +636,63 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
   return moe_forward_timed(cfg, tokens, x, w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
                            ws_up, ws_up_scale, ws_down, ws_down_scale, y, topk_idx, topk_w,
                            expert_counts, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_rmsnorm(const moe_config* cfg, int64_t tokens, const void* x, const void* weight,
+                       float eps, void* out, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (tokens < 0 || !std::isfinite(eps) || eps < 0.0f) return MOE_ERR_INVALID_ARG;
+  if (tokens == 0) return MOE_OK;
+  const void* ptrs[] = {x, weight, out};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  NormArgs a{x, weight, out, tokens, cfg->hidden, eps};
+  return hip_status(
+      launch_rmsnorm(a, cfg->act_dtype == MOE_BF16, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_block_workspace_size(const moe_config* cfg, int64_t tokens, size_t* bytes) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  Carver cv(nullptr);
+  carve_forward(cv, *cfg, tokens);
+  cv.take<char>(norm_bytes(*cfg, tokens));
+  *bytes = cv.used;
+  return MOE_OK;
+}
+
+moe_status moe_block_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
+                                   const void* norm_weight, float eps, const void* w_gate,
+                                   const float* e_bias, const void* w_up,
+                                   const void* w_up_scale, const void* w_down,
+                                   const void* w_down_scale, const void* ws_up,
+                                   const void* ws_up_scale, const void* ws_down,
+                                   const void* ws_down_scale, void* out, int32_t* topk_idx,
+                                   float* topk_w, int32_t* expert_counts, void* workspace,
+                                   size_t workspace_bytes, void* stream, void* const* ev) {
+  if (!norm_weight || !aligned16(norm_weight) || !std::isfinite(eps) || eps < 0.0f)
+    return MOE_ERR_INVALID_ARG;
+  const LayerWeights w{w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
+                       ws_up, ws_up_scale, ws_down, ws_down_scale};
+  return run_forward(cfg, tokens, x, norm_weight, eps, w, out, topk_idx, topk_w, expert_counts,
+                     workspace, workspace_bytes, stream, ev);
+}
+
+moe_status moe_block_forward(const moe_config* cfg, int64_t tokens, const void* x,
+                             const void* norm_weight, float eps, const void* w_gate,
+                             const float* e_bias, const void* w_up, const void* w_up_scale,
+                             const void* w_down, const void* w_down_scale, const void* ws_up,
+                             const void* ws_up_scale, const void* ws_down,
+                             const void* ws_down_scale, void* out, int32_t* topk_idx,
+                             float* topk_w, int32_t* expert_counts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return moe_block_forward_timed(cfg, tokens, x, norm_weight, eps, w_gate, e_bias, w_up,
+                                 w_up_scale, w_down, w_down_scale, ws_up, ws_up_scale, ws_down,
+                                 ws_down_scale, out, topk_idx, topk_w, expert_counts, workspace,
+                                 workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -332,7 +332,9 @@ __global__ __launch_bounds__(PM_THREADS) void schedule_kernel(ScheduleArgs p) {
       p.n_groups, p.spec, tiles, tmp, &carry);
 }
 
-// y[t] = sum_j w[t,j] * y_perm[slot_pos[t*k+j]] (+ shared[t]), fp32, rounded once.
+// y[t] = sum_j w[t,j] * y_perm[slot_pos[t*k+j]] (+ shared[t]) (+ residual[t]),
+// fp32, rounded once.  y may alias the residual: a thread reads its own
+// elements before writing them.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
   // one float4 of one token per thread, over a flat grid of tokens x columns
@@ -371,6 +373,21 @@ __global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
         __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p.shared + t * p.hidden) + c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = acc[q] + sv[q];
+  }
+  if (p.residual) {  // the block's residual stream, added before the one rounding
+    if (BF16_OUT) {
+      const uint2 rv =
+          reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.residual) + t * p.hidden)[c];
+      acc[0] = acc[0] + __uint_as_float(rv.x << 16);
+      acc[1] = acc[1] + __uint_as_float(rv.x & 0xFFFF0000u);
+      acc[2] = acc[2] + __uint_as_float(rv.y << 16);
+      acc[3] = acc[3] + __uint_as_float(rv.y & 0xFFFF0000u);
+    } else {
+      const f32x4_t rv =
+          reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p.residual) + t * p.hidden)[c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = acc[q] + rv[q];
+    }
   }
   if (BF16_OUT) {
     uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);

@@ -66,6 +66,7 @@ class Workload:
     seed: int = 0
     shared_dtype: str = None  # shared-expert weights; None = act_dtype
     norm_eps: float = 1e-5    # the block's RMSNorm eps (layer_norm_epsilon)
+    block: bool = False       # measured as the block x + MoE(RMSNorm(x))
 
     @property
     def shared_weight_dtype(self) -> str:
@@ -89,6 +90,9 @@ WORKLOADS = {
                                  bias_boost=(0, 4, 8, 12, 64, 68, 72, 76), bias_boost_value=2.0,
                                  **_NEMOTRON),
     "fp8-T8192": Workload("fp8-T8192", 8192, act_dtype=BF16, expert_dtype=FP8, **_NEMOTRON),
+    # the decode step as the block around the layer: x + MoE(RMSNorm(x))
+    "block-decode-bf16-T32": Workload("block-decode-bf16-T32", 32, act_dtype=BF16,
+                                      expert_dtype=BF16, block=True, **_NEMOTRON),
     # routed and shared experts in 4-bit MXFP4 (W4A16: activations and h stay bf16)
     "decode-fp4-T32": Workload("decode-fp4-T32", 32, act_dtype=BF16, expert_dtype=FP4,
                                shared_dtype=FP4, **_NEMOTRON),

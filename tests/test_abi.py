@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
-    assert binding.lib().moe_abi_version() == 2
+    assert binding.lib().moe_abi_version() == 3
 
 
 def _cfg(**kw):
@@ -132,6 +132,31 @@ def test_null_and_misaligned_pointers_are_refused():
                        fake, None, fake, None, None, None, fake, 1 << 40, None)
     assert st == MOE_ERR_INVALID_ARG  # and so does an fp4 shared expert
     del args
+
+
+def test_block_entry_points_check_on_the_host():
+    L = binding.lib()
+    c = _cfg()
+    fake = ctypes.c_void_p(0x10000)
+    # eps must be finite and non-negative; pointers present
+    assert L.moe_rmsnorm(ctypes.byref(c), 4, fake, fake, -1.0, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(ctypes.byref(c), 4, fake, fake, float("nan"), fake,
+                         None) == MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(ctypes.byref(c), 4, None, fake, 1e-5, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_rmsnorm(ctypes.byref(c), 0, None, None, 1e-5, None, None) == MOE_OK
+    # the block's workspace holds the layer's and T x d normalised rows
+    nb, nl = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.moe_block_workspace_size(ctypes.byref(c), 32, ctypes.byref(nb)) == MOE_OK
+    assert L.moe_workspace_size(ctypes.byref(c), 32, ctypes.byref(nl)) == MOE_OK
+    assert nb.value >= nl.value + 32 * c.hidden * 2
+    # no norm weight; then a workspace one byte short
+    args = [fake] * 11 + [None, None, None, fake]  # weights, out; routing outputs; workspace
+    st = L.moe_block_forward(ctypes.byref(c), 4, fake, None, 1e-5, *args, 1 << 40, None)
+    assert st == MOE_ERR_INVALID_ARG
+    nb4 = ctypes.c_size_t()
+    L.moe_block_workspace_size(ctypes.byref(c), 4, ctypes.byref(nb4))
+    st = L.moe_block_forward(ctypes.byref(c), 4, fake, fake, 1e-5, *args, nb4.value - 1, None)
+    assert st == MOE_ERR_WORKSPACE
 
 
 def test_permute_x_and_x_perm_go_together():
