@@ -78,6 +78,10 @@ def _ws(cfg, T=32):
     (dict(expert_dtype=MOE_FP8_E4M3), MOE_OK),
     (dict(expert_dtype=MOE_FP4_E2M1), MOE_OK),
     (dict(expert_dtype=MOE_FP4_E2M1, shared_dtype=MOE_FP4_E2M1), MOE_OK),
+    (dict(expert_dtype=MOE_FP4_E2M1, hidden=8192), MOE_OK),             # the largest fp4 K
+    (dict(expert_dtype=MOE_FP4_E2M1, hidden=8256), MOE_ERR_UNSUPPORTED),
+    (dict(expert_dtype=MOE_FP4_E2M1, shared_dtype=MOE_FP4_E2M1, shared_inter=8256),
+     MOE_ERR_UNSUPPORTED),
 ])
 def test_config_checks(kw, status):
     assert _ws(_cfg(**kw))[0] == status

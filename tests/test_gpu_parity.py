@@ -40,10 +40,12 @@ FP4_MANY_ROWS = Workload("many-rows-fp4-T600", 600, 128, 16, 2, 1, 2, 128, 192, 
                          seed=32, shared_dtype="fp4")
 BIG_GROUPS_FP4 = Workload("big-groups-fp4-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp4",
                           seed=33, shared_dtype="fp4")
+# the largest K of fp4 weights: a 64-row tile's block scales fill the LDS they are staged in
+FP4_MAX_K = Workload("fp4-max-k-T20", 20, 8192, 16, 4, 1, 2, 256, 0, "bf16", "fp4", seed=34)
 
 SMALL = [WORKLOADS["tiny-f32-T64"], RAGGED_BF16, RAGGED_FP8, PLAIN_TOPK, ALL_GROUPS, WHOLE_GROUP,
          BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE, BIG_GROUPS_BF16, BIG_GROUPS_FP8, SHORT_K,
-         RAGGED_FP4, FP4_BF16_SHARED, FP4_MANY_ROWS, WORKLOADS["decode-fp4-T32"]]
+         RAGGED_FP4, FP4_BF16_SHARED, FP4_MANY_ROWS, WORKLOADS["decode-fp4-T32"], FP4_MAX_K]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -361,3 +363,37 @@ def test_permute_many_chunks_matches_the_oracle(T, k, E, skew):
     np.testing.assert_array_equal(perm["offsets"].cpu().numpy(), offsets)
     np.testing.assert_array_equal(perm["sorted_slot"].cpu().numpy(), sorted_slot)
     np.testing.assert_array_equal(perm["slot_pos"].cpu().numpy(), slot_pos)
+
+
+def test_decode_rows_past_32_bit_offsets():
+    """Activations over 2 GiB: the decode tiles fall back from the buffer-load
+    kernel (32-bit offsets) to gemm_kernel, with the same bits per row as the
+    buffer-load kernel on the same rows gathered into a small array."""
+    d, I, E = 2688, 1856, 4
+    a_rows = (1 << 31) // (2 * d) + 2000  # just past 2 GiB of bf16 rows
+    print(f"case a_rows={a_rows}", flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn((a_rows, d), generator=gen, device="cuda").to(torch.bfloat16)
+    w_up = (torch.randn((E, I, d), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    w_down = (torch.randn((E, d, I), generator=gen, device="cuda") * 0.02).to(torch.bfloat16)
+    rng = np.random.default_rng(4)
+    src = np.concatenate([rng.integers(a_rows - 3000, a_rows, 36), [0, 1, 2, a_rows - 1]])
+    src = src.astype(np.int32)
+    off = torch.tensor([0, 9, 21, 30, 40], dtype=torch.int32, device="cuda")  # ~10 rows each
+    cfg = binding.config_from(dataclasses.replace(WORKLOADS["decode-bf16-T32"], n_experts=16,
+                                                  n_group=4, top_k=2))
+    idx = torch.from_numpy(src).cuda()
+    big = binding.expert_ffn(cfg, w_up, w_down, a, off, 40, row_index=idx, w_dtype="bf16")
+    a_small = a[idx.long()].contiguous()
+    small = binding.expert_ffn(cfg, w_up, w_down, a_small, off, 40, w_dtype="bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(big, small)
+    mats = np.repeat(np.arange(E), [9, 12, 9, 10])
+    pick = np.array([0, 10, 25, 39])
+    a_np = a_small.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.ffn_rows(a_np, "bf16", pick, mats[pick],
+                          w_up.view(torch.int16).cpu().numpy().view(np.uint16),
+                          w_down.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    assert_close_rms(to_f64(big)[pick], ref, "rows past 2 GiB")
+    del a
+    torch.cuda.empty_cache()
