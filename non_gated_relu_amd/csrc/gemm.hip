@@ -34,21 +34,6 @@
 
 #include "internal.hpp"
 
-#ifndef MOE_FP8_RING
-#define MOE_FP8_RING 1
-#endif
-#ifndef MOE_RING_WAVES
-#define MOE_RING_WAVES 8
-#endif
-#ifndef MOE_DEC_KERNEL
-#define MOE_DEC_KERNEL 1
-#endif
-#ifndef MOE_DEC_DEPTH
-#define MOE_DEC_DEPTH 2
-#endif
-#ifndef MOE_DEC_KB
-#define MOE_DEC_KB 256
-#endif
 namespace moe {
 
 namespace {
@@ -1192,11 +1177,9 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
     // decode tiles; its buffer offsets are 32-bit, else gemm_kernel below
     const bool fits = p.prob[0].a_rows * int64_t(p.prob[0].k) * 2 <= 0x7fffffff &&
                       p.prob[1].a_rows * int64_t(p.prob[1].k) * 2 <= 0x7fffffff;
-    if (shape.bm == 16 && fits && MOE_DEC_KERNEL) {
-      if (shape.bn == 64)
-        return launch_k(gemm_dec_kernel<EPI, 64, MOE_DEC_DEPTH, MOE_DEC_KB>, g, dim3(256), stream,
-                        t, p);
-    }
+    // two stages of 256-byte rows in flight
+    if (shape.bm == 16 && shape.bn == 64 && fits)
+      return launch_k(gemm_dec_kernel<EPI, 64, 2, 256>, g, dim3(256), stream, t, p);
   }
   if (shape.bm == 16 && shape.bn == 64)
     return launch_k(gemm_kernel<KIND, 16, 64, 1, 4, EPI, 256, 0>, g, dim3(256), stream, t, p);
@@ -1204,16 +1187,11 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
     return launch_k(gemm_kernel<KIND, 64, 128, 2, 2, EPI, 256, 0>, g, dim3(256), stream, t, p);
   if constexpr (KIND == K_BF16) {
     if (shape.bm == RG_BM)
-      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES, 4>, g,
-                      dim3(MOE_RING_WAVES * WAVE), stream, t, p);
+      return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
   }
   if constexpr (KIND == K_FP8) {
-    if (shape.bm == RG_BM && MOE_FP8_RING)
-      return launch_k(gemm_ring_kernel<KIND, EPI, MOE_RING_WAVES, 4>, g, dim3(MOE_RING_WAVES * WAVE),
-                      stream, t, p);
-    if (shape.bm == 256)
-      return launch_k(gemm_kernel<KIND, 256, 256, 2, 4, EPI, 512, 32>, g, dim3(512), stream, t,
-                      p);
+    if (shape.bm == RG_BM)
+      return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
   }
   // two workgroups per CU: 64 tiles per XCD in flight
   return launch_k(gemm_kernel<KIND, 128, 128, 2, 2, EPI, 256, 64>, g, dim3(256), stream, t, p);
