@@ -145,10 +145,20 @@ __device__ __forceinline__ int xcd_tile_order(int b, int grid, int per_xcd) {
 
 template <int BM, int BN>
 __device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t, int bid) {
-  const int mt = bid / pa.n_tiles;
-  const int nt = bid - mt * pa.n_tiles;
+  int mt = bid / pa.n_tiles;
+  int nt = bid - mt * pa.n_tiles;
   int gs;
   if (pa.sched) {
+    // the first problem's M tiles take n_tiles workgroups each, the second's
+    // n_tiles2
+    const int first = pa.sched[1];
+    if (mt >= first) {
+      if (pa.n_tiles2 == 0) return false;
+      const int b2 = bid - first * pa.n_tiles;
+      const int m2 = b2 / pa.n_tiles2;
+      mt = first + m2;
+      nt = b2 - m2 * pa.n_tiles2;
+    }
     if (mt >= pa.sched[0]) return false;
     gs = pa.sched[2 + 2 * mt];
     t.m0 = pa.sched[3 + 2 * mt];
@@ -1223,9 +1233,9 @@ int64_t max_mtiles(int64_t rows, int groups, int bm) {
   return rows < bound ? rows : bound;
 }
 
-hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_bound,
-                       hipStream_t stream, Timing t) {
-  const int64_t grid64 = mtiles_bound * p.n_tiles;
+hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_first,
+                       int64_t mtiles_second, hipStream_t stream, Timing t) {
+  const int64_t grid64 = mtiles_first * p.n_tiles + mtiles_second * p.n_tiles2;
   if (grid64 <= 0) return hipSuccess;
   if (grid64 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   const unsigned grid = static_cast<unsigned>(grid64);

@@ -47,7 +47,8 @@ struct RouteArgs {
   float scale;
 };
 
-// M-tile schedule of a grouped GEMM: sched[0] = tile count; entry i at
+// M-tile schedule of a grouped GEMM: sched[0] = tile count, sched[1] = the
+// tiles of the first problem's groups (they come first); entry i at
 // sched[2+2i] = group, sched[3+2i] = first problem row.  Tiles of a group are
 // consecutive and groups come in order; the optional extra group (index
 // n_groups) covers rows [0, extra_rows) of the second problem.
@@ -136,12 +137,16 @@ struct GemmProblem {
 };
 
 // A launch: the groups of prob[0], plus (schedule group index n_groups) the
-// single group of prob[1] when the schedule holds one.
+// single group of prob[1] when the schedule holds one.  Workgroups first
+// cover the M tiles of prob[0], n_tiles each, then those of prob[1],
+// n_tiles2 each, so that no workgroup of a launch whose problems differ in N
+// is left without a tile.
 struct GemmArgs {
   GemmProblem prob[2];
   const int32_t* sched;
   int n_groups;
-  int n_tiles;               // N tiles of the launch (the larger of the two problems)
+  int n_tiles;               // N tiles of prob[0]
+  int n_tiles2;              // N tiles of prob[1] (0: no second problem)
 };
 
 struct QuantArgs {
@@ -185,8 +190,9 @@ hipError_t launch_rmsnorm(const NormArgs& p, bool bf16, hipStream_t stream, Timi
 GemmShape pick_gemm_shape(int kind, int64_t rows, int groups);
 // Upper bound of the M tiles a schedule of this shape can hold.
 int64_t max_mtiles(int64_t rows, int groups, int bm);
-// Launch one grouped GEMM (schedule already built for shape.bm).
-hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_bound,
-                       hipStream_t stream, Timing t = {});
+// Launch one grouped GEMM (schedule already built for shape.bm): at most
+// `mtiles_first` M tiles of prob[0] and `mtiles_second` of prob[1].
+hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, int64_t mtiles_first,
+                       int64_t mtiles_second, hipStream_t stream, Timing t = {});
 
 }  // namespace moe

@@ -139,14 +139,16 @@ struct Mlp {
 // single-group problem).
 struct FfnPlan {
   GemmShape shape;  // both projections
-  int64_t mtiles;
+  int64_t mtiles_first;   // bound of the routed (or only) family's M tiles
+  int64_t mtiles_extra;   // M tiles of the extra single-group family
+  int64_t mtiles() const { return mtiles_first + mtiles_extra; }
 };
 
 FfnPlan plan_ffn(int32_t w_dtype, int64_t rows, int n_mats, int64_t extra_rows) {
   FfnPlan f;
   f.shape = pick_gemm_shape(kind_of(w_dtype), rows, n_mats);
-  f.mtiles = max_mtiles(rows, n_mats, f.shape.bm) +
-             (extra_rows > 0 ? (extra_rows + f.shape.bm - 1) / f.shape.bm : 0);
+  f.mtiles_first = max_mtiles(rows, n_mats, f.shape.bm);
+  f.mtiles_extra = extra_rows > 0 ? (extra_rows + f.shape.bm - 1) / f.shape.bm : 0;
   return f;
 }
 
@@ -214,7 +216,7 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   const FfnPlan f = plan_ffn(m.w_dtype, m.rows, m.n_mats, extra_rows);
   if (!have_sched) {
     ScheduleArgs sp{m.offsets, m.rows, m.n_mats,
-                    ScheduleSpec{sched, extra_rows, f.shape.bm, static_cast<int>(f.mtiles)}};
+                    ScheduleSpec{sched, extra_rows, f.shape.bm, static_cast<int>(f.mtiles())}};
     if (launch_schedule(sp, s) != hipSuccess) return MOE_ERR_HIP;
   }
   const int kind = kind_of(m.w_dtype);
@@ -227,8 +229,10 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   if (extra) up.prob[1] = up_problem(*extra, hidden);
   up.sched = sched;
   up.n_groups = m.n_mats;
-  up.n_tiles = (std::max(m.inter, extra ? extra->inter : 0) + f.shape.bn - 1) / f.shape.bn;
-  if (launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles, s, tm.up) != hipSuccess)
+  up.n_tiles = (m.inter + f.shape.bn - 1) / f.shape.bn;
+  up.n_tiles2 = extra ? (extra->inter + f.shape.bn - 1) / f.shape.bn : 0;
+  if (launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles_first, f.mtiles_extra, s, tm.up) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   if (kind == K_FP8) {
     QuantArgs q{m.h, m.hq, m.hs, m.rows, m.inter, 0};
@@ -240,7 +244,9 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   dn.sched = sched;
   dn.n_groups = m.n_mats;
   dn.n_tiles = (hidden + f.shape.bn - 1) / f.shape.bn;
-  if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles, s, tm.down) != hipSuccess)
+  dn.n_tiles2 = extra ? dn.n_tiles : 0;
+  if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles_first, f.mtiles_extra, s, tm.down) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -316,10 +322,10 @@ Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
     carve_mlp_buffers(cv, sh, c.hidden);
   }
   f.plan = plan_ffn(r.w_dtype, r.rows, r.n_mats, f.fused_shared ? T : 0);
-  f.sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.plan.mtiles)));
+  f.sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.plan.mtiles())));
   if (c.shared_inter > 0 && !f.fused_shared) {
     const FfnPlan ps = plan_ffn(c.shared_dtype, T, 1, 0);
-    f.shared_sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(ps.mtiles)));
+    f.shared_sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(ps.mtiles())));
   }
   return f;
 }
@@ -357,7 +363,7 @@ Mlp standalone_mlp(int32_t n_mats, int32_t inter, int32_t w_dtype, int64_t a_row
 
 size_t carve_standalone(Carver& cv, Mlp& m, int hidden, int32_t** sched) {
   const FfnPlan f = plan_ffn(m.w_dtype, m.rows, m.n_mats, 0);
-  *sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.mtiles)));
+  *sched = cv.take<int32_t>(sizeof(int32_t) * (2 + 2 * size_t(f.mtiles())));
   carve_mlp_buffers(cv, m, hidden);
   return cv.used;
 }
@@ -436,7 +442,7 @@ moe_status run_forward(const moe_config* cfg, int64_t tokens, const void* x,
       hipSuccess)
     return MOE_ERR_HIP;
   const ScheduleSpec spec{f.sched, f.fused_shared ? tokens : 0, f.plan.shape.bm,
-                          static_cast<int>(f.plan.mtiles)};
+                          static_cast<int>(f.plan.mtiles())};
   if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
                        f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
     return st;

@@ -165,7 +165,10 @@ __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp,
       sp.sched[3 + 2 * at] = j * sp.bm;
     }
   }
-  if (threadIdx.x == 0) sp.sched[0] = min(*carry + extra, sp.max_tiles);
+  if (threadIdx.x == 0) {
+    sp.sched[0] = min(*carry + extra, sp.max_tiles);
+    sp.sched[1] = min(*carry, sp.max_tiles);
+  }
   __syncthreads();
 }
 

@@ -152,7 +152,7 @@ hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stre
     const GemmShape shape = p.tokens <= 8192 ? GemmShape{16, 128, true} : GemmShape{64, 128};
     g.n_tiles = (p.n_experts + shape.bn - 1) / shape.bn;
     const int64_t mtiles = (p.tokens + shape.bm - 1) / shape.bm;
-    e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, stream, first);
+    e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, 0, stream, first);
   }
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>((p.tokens + 3) / 4));
