@@ -170,6 +170,20 @@ moe_status moe_expert_ffn(const moe_config* cfg, int32_t n_mats, int32_t inter, 
                           const void* w_down, const void* w_down_scale, float* out,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* The per-row quantiser of the fp8 expert path (moe_expert_ffn with
+ * MOE_FP8_E4M3 weights applies it to the rows of a before the up GEMM and to
+ * the fp32 rows of h before the down GEMM).  For each row r, in fp32:
+ *     s_r = max_i |in[r,i]| / 448          (1 when the row is all zeros)
+ *     q[r,i] = e4m3(in[r,i] / s_r)         (correctly rounded division; the
+ *              OCP 8-bit floating point specification's E4M3 encoding,
+ *              nearest even, saturating at +-448; a zero result is +0)
+ * so that q[r,i] * s_r approximates in[r,i].
+ *   in_dtype MOE_F32 or MOE_BF16; in [rows, cols] of in_dtype; q [rows, cols]
+ *   uint8 out; scale [rows] fp32 out.  cols a positive multiple of 8.
+ *   rows == 0 enqueues nothing. */
+moe_status moe_quantize_rows(int32_t in_dtype, int64_t rows, int32_t cols, const void* in,
+                             uint8_t* q, float* scale, void* stream);
+
 /* Weighted combine (exo commit "Add support for Nemotron sharding": the shared
  * expert's output joins the routed sum before the mixer's single reduction):
  *     y[t] = sum_{j ascending} topk_w[t,j] * y_perm[slot_pos[t*k+j]] + shared_out[t]

@@ -75,11 +75,12 @@ def lib() -> ctypes.CDLL:
         L.moe_block_forward.argtypes = ([_cfgp, _i64, _vp, _vp, ctypes.c_float] +
                                         [_vp] * 15 + [ctypes.c_size_t, _vp])
         L.moe_block_forward_timed.argtypes = L.moe_block_forward.argtypes + [_vp]
+        L.moe_quantize_rows.argtypes = [_i32, _i64, _i32, _vp, _vp, _vp, _vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
                      "moe_forward", "moe_forward_timed", "moe_rmsnorm",
                      "moe_block_workspace_size", "moe_block_forward",
-                     "moe_block_forward_timed"):
+                     "moe_block_forward_timed", "moe_quantize_rows"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -242,6 +243,20 @@ def block_workspace_size(cfg: MoeConfig, tokens: int) -> int:
     _check(lib().moe_block_workspace_size(ctypes.byref(cfg), tokens, ctypes.byref(n)),
            "moe_block_workspace_size")
     return n.value
+
+
+def quantize_rows(x, q=None, scale=None):
+    """Per-row e4m3 codes and fp32 scales of x [rows, cols] (fp32 or bf16):
+    moe_quantize_rows."""
+    rows, cols = x.shape
+    dt = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}.get(x.dtype)
+    if dt is None:
+        raise TypeError(f"quantize_rows takes fp32 or bf16 rows, not {x.dtype}")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device) if q is None else q
+    scale = torch.empty(rows, dtype=torch.float32, device=x.device) if scale is None else scale
+    _check(lib().moe_quantize_rows(dt, rows, cols, _p(x), _p(q), _p(scale), _stream()),
+           "moe_quantize_rows")
+    return q, scale
 
 
 def rmsnorm(cfg: MoeConfig, x, weight, eps: float, out=None):

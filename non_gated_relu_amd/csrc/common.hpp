@@ -28,28 +28,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-// binary32 -> OCP e4m3fn code (bias 7, 3 mantissa bits, largest finite 448),
-// nearest even, magnitudes at or above 448 saturate to 448.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (a >= 0x43E00000u) {            // |f| >= 448 (and inf)
-    code = 0x7Eu;
-  } else if (a < 0x3C800000u) {      // |f| < 2^-6: multiples of 2^-9
-    code = static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.0f));  // 8 -> 2^-6, still right
-  } else {
-    uint32_t e = (a >> 23) - 127 + 7;
-    uint32_t keep = (a >> 20) & 7u;
-    uint32_t rem = a & 0xFFFFFu;
-    uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (keep & 1u));
-    code = (e << 3) + keep + up;
-    code = code > 0x7Eu ? 0x7Eu : code;
-  }
-  return code == 0 ? 0u : (code | sign);
-}
-
 // ---------------------------------------------------------------- waves
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }

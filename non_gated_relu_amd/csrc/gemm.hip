@@ -1096,9 +1096,14 @@ __global__ __launch_bounds__(256) void gemm_dec_kernel(GemmArgs pa) {
     store_block<K_BF16, EPI>(t, acc[j], t.m0 + 4 * lgrp, t.n0 + wave * (BN / 4) + 16 * j + lrow);
 }
 
-// One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale.
-// Rows up to QV_MAX * 256 columns are read once into registers (all loads in
-// flight together); longer rows are read twice.
+// One wave per row: amax, scale = amax / 448 (0 -> 1), e4m3 codes of v / scale
+// (the division correctly rounded, as the compiler emits it without fast-math
+// flags).  v / scale is clamped to +-448 (it exceeds 448 by more than an ulp
+// only when the scale is an fp32 subnormal), then v_cvt_pk_fp8_f32 rounds it
+// to nearest even into OCP e4m3fn (gfx950's fp8 format); a code that rounds
+// to zero is written as +0 (the instruction keeps the sign).  Rows up to
+// QV_MAX * 256 columns are read once into registers (all loads in flight
+// together); longer rows are read twice.
 constexpr int QV_MAX = 12;
 __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
   const int64_t row = int64_t(blockIdx.x) * 4 + threadIdx.x / WAVE;
@@ -1124,10 +1129,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(QuantArgs p) {
     }
   };
   auto quant4 = [&](const float* v, float s) {
-    uint32_t w = 0;
+    float r[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) w |= f32_to_e4m3(v[q] / s) << (8 * q);
-    return w;
+    for (int q = 0; q < 4; ++q) r[q] = __builtin_amdgcn_fmed3f(v[q] / s, -448.0f, 448.0f);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w, true);
+    // bit 7 of each byte of m: the byte's magnitude bits are not all zero
+    const uint32_t u = static_cast<uint32_t>(w);
+    const uint32_t m = (u & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+    return u & (0x7F7F7F7Fu | (m & 0x80808080u));
   };
   auto row_scale = [&](float amax) {
 #pragma unroll
@@ -1250,6 +1260,7 @@ hipError_t launch_gemm(const GemmArgs& p, int kind, int epi, GemmShape shape, in
 hipError_t launch_quant(const QuantArgs& p, hipStream_t stream, Timing t) {
   if (p.rows <= 0) return hipSuccess;
   const int64_t blocks = (p.rows + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   return launch_k(quant_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), stream, t, p);
 }
 

@@ -465,7 +465,7 @@ moe_status run_forward(const moe_config* cfg, int64_t tokens, const void* x,
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 3; }
+int32_t moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(moe_status st) {
   switch (st) {
@@ -642,6 +642,18 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
   return moe_forward_timed(cfg, tokens, x, w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
                            ws_up, ws_up_scale, ws_down, ws_down_scale, y, topk_idx, topk_w,
                            expert_counts, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_quantize_rows(int32_t in_dtype, int64_t rows, int32_t cols, const void* in,
+                             uint8_t* q, float* scale, void* stream) {
+  if (in_dtype != MOE_F32 && in_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (rows < 0 || cols <= 0 || cols % 8) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  const void* ptrs[] = {in, q, scale};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return MOE_ERR_INVALID_ARG;
+  QuantArgs a{in, q, scale, rows, cols, in_dtype == MOE_BF16 ? 1 : 0};
+  return hip_status(launch_quant(a, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_rmsnorm(const moe_config* cfg, int64_t tokens, const void* x, const void* weight,

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
-    assert binding.lib().moe_abi_version() == 3
+    assert binding.lib().moe_abi_version() == 4
 
 
 def _cfg(**kw):
@@ -161,6 +161,19 @@ def test_block_entry_points_check_on_the_host():
     L.moe_block_workspace_size(ctypes.byref(c), 4, ctypes.byref(nb4))
     st = L.moe_block_forward(ctypes.byref(c), 4, fake, fake, 1e-5, *args, nb4.value - 1, None)
     assert st == MOE_ERR_WORKSPACE
+
+
+def test_quantize_rows_checks_on_the_host():
+    L = binding.lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert L.moe_quantize_rows(MOE_FP8_E4M3, 4, 64, fake, fake, fake, None) == MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_rows(MOE_BF16, -1, 64, fake, fake, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(MOE_BF16, 4, 60, fake, fake, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(MOE_F32, 4, 0, fake, fake, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(MOE_F32, 4, 64, fake, None, fake, None) == MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(MOE_F32, 4, 64, ctypes.c_void_p(0x10004), fake, fake,
+                               None) == MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(MOE_BF16, 0, 64, None, None, None, None) == MOE_OK
 
 
 def test_permute_x_and_x_perm_go_together():
