@@ -224,32 +224,64 @@ __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(PermuteArgs p)
 
 // Pass 2 (one workgroup): per-expert totals, offsets, each chunk's base, and
 // the GEMM schedule.  The chunk counts are scanned in LDS when they fit
-// (n_chunks * E <= PM_SCAN_LDS), with coalesced loads and stores; otherwise
-// each expert's column is walked in global memory.
+// (n_chunks * E <= PM_SCAN_LDS), with coalesced loads and stores: H =
+// PM_THREADS / E threads share an expert's column, each scanning a run of
+// consecutive chunks, and the runs' totals are then added in order.
+// Otherwise each expert's column is walked in global memory.
 constexpr int PM_SCAN_LDS = 16384;
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p) {
   __shared__ int32_t off[1024];
   __shared__ int32_t cnt[1024];
   __shared__ int32_t tiles[1024];
   __shared__ int32_t tmp[PM_THREADS];
+  __shared__ int32_t run_total[PM_THREADS];
+  __shared__ int32_t run_base[PM_THREADS];
   __shared__ int32_t bc[PM_SCAN_LDS];
   __shared__ int32_t carry;
   const int E = p.n_experts;
   const int nb = p.n_chunks * E;
   const bool in_lds = nb <= PM_SCAN_LDS;
+  const int H = E <= PM_THREADS ? PM_THREADS / E : 1;  // threads per expert column
+  const int per = (p.n_chunks + H - 1) / H;            // chunks per run
   if (in_lds) {
-    for (int i = threadIdx.x; i < nb; i += PM_THREADS) bc[i] = p.block_counts[i];
+    constexpr int B = 8;  // loads in flight per thread
+    for (int i0 = 0; i0 < nb; i0 += B * PM_THREADS) {
+      int32_t v[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int i = i0 + u * PM_THREADS + threadIdx.x;
+        v[u] = i < nb ? p.block_counts[i] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < B; ++u) {
+        const int i = i0 + u * PM_THREADS + threadIdx.x;
+        if (i < nb) bc[i] = v[u];
+      }
+    }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+    const int e = threadIdx.x % E;
+    const int h = threadIdx.x / E;  // run h of expert e's column (none when h >= H)
+    if (h < H) {
       int32_t total = 0;
-      for (int b = 0; b < p.n_chunks; ++b) {
+      const int b_end = min((h + 1) * per, p.n_chunks);
+      for (int b = h * per; b < b_end; ++b) {
         const int32_t v = bc[b * E + e];
-        bc[b * E + e] = total;  // the chunk's base inside expert e
+        bc[b * E + e] = total;  // the chunk's base inside its run
         total += v;
       }
-      p.expert_counts[e] = total;
-      off[e] = total;
-      cnt[e] = total;
+      run_total[h * E + e] = total;
+    }
+    __syncthreads();
+    if (h < H) {
+      int32_t before = 0;
+      for (int j = 0; j < h; ++j) before += run_total[j * E + e];
+      run_base[h * E + e] = before;
+      if (h == H - 1) {
+        const int32_t total = before + run_total[h * E + e];
+        p.expert_counts[e] = total;
+        off[e] = total;
+        cnt[e] = total;
+      }
     }
   } else {
     constexpr int B = 8;  // chunk counts loaded per batch
@@ -277,7 +309,11 @@ __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p)
   block_exclusive_scan(off, E, tmp);
   for (int e = threadIdx.x; e < E; e += PM_THREADS) p.expert_offsets[e] = off[e];
   if (in_lds) {
-    for (int i = threadIdx.x; i < nb; i += PM_THREADS) p.block_counts[i] = bc[i] + off[i % E];
+    for (int i = threadIdx.x; i < nb; i += PM_THREADS) {
+      const int b = i / E;
+      const int e = i - b * E;
+      p.block_counts[i] = bc[i] + run_base[(b / per) * E + e] + off[e];
+    }
   } else {
     for (int e = threadIdx.x; e < E; e += PM_THREADS)
       for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];

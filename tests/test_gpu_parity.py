@@ -338,7 +338,8 @@ def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
 
 
 @pytest.mark.parametrize("T,k,E,skew", [(1500, 6, 128, False), (4097, 6, 128, True),
-                                        (16384, 6, 128, True), (3000, 3, 16, False)])
+                                        (16384, 6, 128, True), (3000, 3, 16, False),
+                                        (2000, 4, 48, True), (5000, 8, 256, False)])
 def test_permute_many_chunks_matches_the_oracle(T, k, E, skew):
     """The multi-workgroup permute (slots beyond one workgroup's share) gives
     exactly the oracle's stable grouping, counts and offsets."""
