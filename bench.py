@@ -177,6 +177,10 @@ def main():
                     help="wall time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (default: the step replayed from a HIP graph)")
+    ap.add_argument("--evict-mb", type=int, default=512,
+                    help="after the timed region, repeat the eager steps with a read of this "
+                         "many MB between them (outside their events), so that nothing of one "
+                         "step stays in the 256 MB Infinity Cache for the next (0 = skip)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run 10 device-to-device copies of this many bytes (a "
                          "reference kernel for calibrating HBM byte counters)")
@@ -256,6 +260,26 @@ def main():
         graph_s = time.perf_counter() - t0
         total_s = graph_s
 
+    # cache check: the eager steps again, each after reading a buffer larger than
+    # the Infinity Cache (a read, so no dirty lines are left to write back)
+    cache_check = None
+    if args.evict_mb > 0:
+        big = torch.ones(args.evict_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        sink = torch.zeros((), dtype=torch.float32, device=dev)
+        evs2 = [binding.StageEvents() for _ in range(steps)]
+        for i in range(steps):
+            sink += big.sum()
+            run(evs2[i])
+        torch.cuda.synchronize()
+        ev_stage = {s: 0.0 for s in stages}
+        for e in evs2:
+            for s, ms in e.elapsed_ms(stages).items():
+                ev_stage[s] += ms / steps
+        cache_check = {"evict": f"{args.evict_mb} MB read before each eager step",
+                       "stages_ms_sum": round(sum(stage_ms.values()), 5),
+                       "stages_ms_sum_after_evict": round(sum(ev_stage.values()), 5)}
+        del big
+
     counts = layer.expert_counts.cpu().numpy()
     active = int((counts > 0).sum())
     work = stage_work(wl, active)
@@ -308,6 +332,8 @@ def main():
             "eager_ms_per_step": 1e3 * eager_s / steps,
             "roofline": roofline, "layer": layer_fig,
             "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
+    if cache_check:
+        line["cache_check"] = cache_check
     if args.cpu_seconds > 0:
         y_np = y.float().cpu().numpy()
         idx_np = layer.topk_idx[:wl.tokens].cpu().numpy()
