@@ -149,17 +149,25 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t, int bid
   int nt = bid - mt * pa.n_tiles;
   int gs;
   if (pa.sched) {
-    // the first problem's M tiles take n_tiles workgroups each, the second's
-    // n_tiles2
+    // the first problem's M tiles take n_tiles workgroups each and the
+    // second's n_tiles2; with second_first the second problem's come first
     const int first = pa.sched[1];
-    if (mt >= first) {
-      if (pa.n_tiles2 == 0) return false;
-      const int b2 = bid - first * pa.n_tiles;
-      const int m2 = b2 / pa.n_tiles2;
+    const int n_second = pa.sched[0] - first;
+    const int b2 = bid - (pa.second_first ? n_second * pa.n_tiles2 : first * pa.n_tiles);
+    const bool in_second = pa.second_first ? b2 < 0 : b2 >= 0;
+    if (in_second) {
+      if (n_second <= 0) return false;  // (then n_tiles2 may be 0)
+      const int b = pa.second_first ? bid : b2;
+      const int m2 = b / pa.n_tiles2;
+      if (m2 >= n_second) return false;
       mt = first + m2;
-      nt = b2 - m2 * pa.n_tiles2;
+      nt = b - m2 * pa.n_tiles2;
+    } else {
+      const int b = pa.second_first ? b2 : bid;
+      mt = b / pa.n_tiles;
+      nt = b - mt * pa.n_tiles;
+      if (mt >= first) return false;
     }
-    if (mt >= pa.sched[0]) return false;
     gs = pa.sched[2 + 2 * mt];
     t.m0 = pa.sched[3 + 2 * mt];
   } else {  // dense: one group, tiles in row order

@@ -137,16 +137,19 @@ struct GemmProblem {
 };
 
 // A launch: the groups of prob[0], plus (schedule group index n_groups) the
-// single group of prob[1] when the schedule holds one.  Workgroups first
-// cover the M tiles of prob[0], n_tiles each, then those of prob[1],
-// n_tiles2 each, so that no workgroup of a launch whose problems differ in N
-// is left without a tile.
+// single group of prob[1] when the schedule holds one.  Workgroups cover the
+// M tiles of prob[0], n_tiles each, and those of prob[1], n_tiles2 each, so
+// that no workgroup of a launch whose problems differ in N is left without a
+// tile.  prob[0]'s come first, unless second_first: decode launches start
+// the shared expert's tiles (the longest in K of a down projection) first,
+// so that they do not make the tail of the launch.
 struct GemmArgs {
   GemmProblem prob[2];
   const int32_t* sched;
   int n_groups;
   int n_tiles;               // N tiles of prob[0]
   int n_tiles2;              // N tiles of prob[1] (0: no second problem)
+  int second_first;          // prob[1]'s tiles before prob[0]'s
 };
 
 struct QuantArgs {

@@ -231,6 +231,7 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   up.n_groups = m.n_mats;
   up.n_tiles = (m.inter + f.shape.bn - 1) / f.shape.bn;
   up.n_tiles2 = extra ? (extra->inter + f.shape.bn - 1) / f.shape.bn : 0;
+  up.second_first = f.shape.bm == 16;  // decode tiles
   if (launch_gemm(up, kind, EPI_RELU2, f.shape, f.mtiles_first, f.mtiles_extra, s, tm.up) !=
       hipSuccess)
     return MOE_ERR_HIP;
@@ -245,6 +246,7 @@ moe_status run_mlps(int hidden, const Mlp& m, const Mlp* extra, int32_t* sched, 
   dn.n_groups = m.n_mats;
   dn.n_tiles = (hidden + f.shape.bn - 1) / f.shape.bn;
   dn.n_tiles2 = extra ? dn.n_tiles : 0;
+  dn.second_first = up.second_first;
   if (launch_gemm(dn, kind, EPI_PLAIN, f.shape, f.mtiles_first, f.mtiles_extra, s, tm.down) !=
       hipSuccess)
     return MOE_ERR_HIP;
