@@ -240,10 +240,14 @@ def main():
     total_s = time.perf_counter() - t0
 
     per_stage = {s: 0.0 for s in stages}
+    step_sums = []
     for e in evs:
-        for s, ms in e.elapsed_ms(stages).items():
+        ms_e = e.elapsed_ms(stages)
+        step_sums.append(sum(ms_e.values()))
+        for s, ms in ms_e.items():
             per_stage[s] += ms
     stage_ms = {s: per_stage[s] / steps for s in stages}
+    q10, q50, q90 = np.percentile(step_sums, [10, 50, 90])
     eager_s = total_s
 
     # the same step replayed from a HIP graph: no per-kernel launch gaps
@@ -330,6 +334,8 @@ def main():
             "launch": ("hipGraph replay of " if graph_s else "eager ") +
                       ("moe_block_forward" if block else "moe_forward"),
             "eager_ms_per_step": 1e3 * eager_s / steps,
+            "eager_kernel_ms_per_step": {"p10": round(float(q10), 5), "median": round(float(q50), 5),
+                                         "p90": round(float(q90), 5)},
             "roofline": roofline, "layer": layer_fig,
             "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
     if cache_check:
