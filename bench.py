@@ -17,9 +17,11 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -173,6 +175,8 @@ def main():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload at this many tokens instead (a prefix of its rows)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--no-graph", action="store_true",
@@ -208,6 +212,9 @@ def main():
 
     wl = WORKLOADS[args.workload]
     steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+    if args.tokens > 0:
+        wl = dataclasses.replace(wl, tokens=args.tokens,
+                                 name=re.sub(r"T\d+$", f"T{args.tokens}", wl.name))
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
