@@ -65,6 +65,8 @@ enum RouteMode : int { ROUTE_ONE_KERNEL = 0, ROUTE_WAVES = 1, ROUTE_GEMM = 2 };
 // Routing slots the single-workgroup permute handles; beyond, the slots are
 // split into chunks of PM_CHUNK, one workgroup each.
 constexpr int PM_SMALL_MAX = 4096;
+// Logits the fused selection and permute stages in LDS.
+constexpr int SP_MAX_LOGITS = 8192;
 constexpr int PM_CHUNK = 1024;
 
 struct PermuteArgs {
@@ -180,7 +182,15 @@ struct GemmShape {
 // put the logits in p.logits and then run the selection kernel.
 hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stream,
                         Timing t = {});
+// The logits of the ROUTE_WAVES mode only (into p.logits), without selection.
+hipError_t launch_route_logits_waves(const RouteArgs& p, int kind, hipStream_t stream,
+                                     Timing t = {});
 hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t = {});
+// Selection from r.logits and the single-workgroup permute in one launch
+// (p.n_chunks == 1; r and p describe the same tokens; r.tokens * E <=
+// SP_MAX_LOGITS, E % 4 == 0).
+hipError_t launch_select_permute(const RouteArgs& r, const PermuteArgs& p, hipStream_t stream,
+                                 Timing t = {});
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream);
 hipError_t launch_schedule(const ScheduleArgs& p, hipStream_t stream, Timing t = {});
 hipError_t launch_combine(const CombineArgs& p, bool bf16_out, hipStream_t stream, Timing t = {});

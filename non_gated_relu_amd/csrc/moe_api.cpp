@@ -29,6 +29,9 @@ namespace {
 
 constexpr int64_t ROUTE_WAVES_MAX_TOKENS = 64;     // up to here: one wave per logit block
 constexpr int64_t ROUTE_DIRECT_MAX_TOKENS = 2048;  // beyond: router logits as a GEMM
+// up to here moe_forward selects and permutes in one launch (each of its four
+// waves selects at most one token; beyond, two launches are faster)
+constexpr int64_t SELECT_PERMUTE_MAX_TOKENS = 4;
 constexpr size_t ALIGN = 256;
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
@@ -440,14 +443,26 @@ moe_status run_forward(const moe_config* cfg, int64_t tokens, const void* x,
   f.shared.down_scale = c.shared_dtype == MOE_FP4_E2M1 ? w.ws_down_scale : nullptr;
 
   const RouteArgs ra = route_args(c, tokens, xl, w.w_gate, w.e_bias, idx, wts, f.logits);
-  if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
   const ScheduleSpec spec{f.sched, f.fused_shared ? tokens : 0, f.plan.shape.bm,
                           static_cast<int>(f.plan.mtiles())};
-  if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
-                       f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
-    return st;
+  if (tokens <= SELECT_PERMUTE_MAX_TOKENS && route_mode(tokens) == ROUTE_WAVES &&
+      permute_chunks(f.S) == 1 && tokens * c.n_experts <= SP_MAX_LOGITS) {
+    // decode: the logits, then the selection and the permute in one launch
+    // (the permute stage's events time both)
+    const PermuteArgs pa{idx, cnt, f.offsets, f.sorted_slot, f.slot_pos, f.block_counts, f.S, 1,
+                         c.n_experts, spec};
+    if (launch_route_logits_waves(ra, kind_of(c.act_dtype), s, slot(ev, MOE_T_ROUTE)) !=
+            hipSuccess ||
+        launch_select_permute(ra, pa, s, slot(ev, MOE_T_PERMUTE)) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (launch_route(ra, kind_of(c.act_dtype), route_mode(tokens), s, slot(ev, MOE_T_ROUTE)) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    if ((st = do_permute(c, tokens, idx, cnt, f.offsets, f.sorted_slot, f.slot_pos,
+                         f.block_counts, spec, s, slot(ev, MOE_T_PERMUTE))) != MOE_OK)
+      return st;
+  }
   FfnTiming rt{slot(ev, MOE_T_QUANT_X), slot(ev, MOE_T_ROUTED_UP), slot(ev, MOE_T_QUANT_H),
                slot(ev, MOE_T_ROUTED_DOWN)};
   if ((st = run_mlps(c.hidden, f.routed, f.fused_shared ? &f.shared : nullptr, f.sched, true, s,

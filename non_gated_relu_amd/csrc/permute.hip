@@ -8,7 +8,7 @@
 // grouped by expert with a histogram, an exclusive scan and a stable
 // placement (slot ids ascend inside an expert).  No atomics decide an order:
 // LDS integer atomics only count, and ranks inside a wave come from ballots.
-#include "internal.hpp"
+#include "select.hpp"
 
 namespace moe {
 
@@ -174,7 +174,7 @@ __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp,
 
 // Small problems (all slots in one workgroup): histogram, scan, schedule,
 // placement.
-__global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p) {
+__device__ __forceinline__ void permute_small(const PermuteArgs& p) {
   __shared__ int32_t cnt[1024];
   __shared__ int32_t run[1024];
   __shared__ int32_t tiles[1024];
@@ -206,6 +206,45 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p
         },
         E, p.sched, tiles, tmp, &carry);
   place_chunk(ids, 0, n, E, run, wc, p.sorted_slot, p.slot_pos);
+}
+
+__global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p) {
+  permute_small(p);
+}
+
+// Decode-sized calls: the grouped top-k of every token from its logits (each
+// wave takes tokens w, w + 4, ...) and then the permute of their slots, in
+// one launch.  The selection is route.hip's, so the routing is the same; the
+// barrier makes each wave's topk_idx visible to the permute.
+static_assert(PM_THREADS >= RT_MAXE, "one thread per expert stages the bias");
+__global__ __launch_bounds__(PM_THREADS) void select_permute_kernel(RouteArgs r, PermuteArgs p) {
+  __shared__ f32x4_t lds_l[SP_MAX_LOGITS / 4];
+  __shared__ float lds_b[RT_MAXE];
+  __shared__ SelScratch scr[PM_WAVES];
+  // every token's logits and the correction bias into LDS, all loads in
+  // flight together
+  const int n4 = static_cast<int>(r.tokens) * r.n_experts / 4;
+  constexpr int PER = SP_MAX_LOGITS / 4 / PM_THREADS;
+  f32x4_t v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = u * PM_THREADS + threadIdx.x;
+    if (i < n4) v[u] = reinterpret_cast<const f32x4_t*>(r.logits)[i];
+  }
+  const float bias = threadIdx.x < r.n_experts ? r.e_bias[threadIdx.x] : 0.0f;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = u * PM_THREADS + threadIdx.x;
+    if (i < n4) lds_l[i] = v[u];
+  }
+  if (threadIdx.x < r.n_experts) lds_b[threadIdx.x] = bias;
+  __syncthreads();
+  const int wave = threadIdx.x / WAVE;
+  const float* logits = reinterpret_cast<const float*>(lds_l);
+  for (int64_t t = wave; t < r.tokens; t += PM_WAVES)
+    select_one(r, logits + t * r.n_experts, t, scr[wave], lds_b);
+  __syncthreads();
+  permute_small(p);
 }
 
 // Large problems, pass 1: per-chunk expert histogram.
@@ -451,6 +490,12 @@ hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t) {
     return e;
   return launch_k(permute_place_kernel, dim3(p.n_chunks), dim3(PM_THREADS), stream,
                   Timing{nullptr, t.stop}, p);
+}
+
+hipError_t launch_select_permute(const RouteArgs& r, const PermuteArgs& p, hipStream_t stream,
+                                 Timing t) {
+  if (p.slots <= 0) return hipSuccess;
+  return launch_k(select_permute_kernel, dim3(1), dim3(PM_THREADS), stream, t, r, p);
 }
 
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream) {

@@ -103,19 +103,44 @@ __global__ __launch_bounds__(WAVE) void route_logits_kernel(RouteArgs p) {
 }
 
 // Selection from logits [tokens, E] in global memory, one wave per token.
+// The wave stages its token's logits and the correction bias in LDS with the
+// same round trip, so the selection itself touches no global memory.
 __global__ __launch_bounds__(256) void route_select_kernel(RouteArgs p) {
   __shared__ float lds_l[4][RT_MAXE];
+  __shared__ float lds_b[4][RT_MAXE];
   __shared__ SelScratch scr[4];
   const int wave = threadIdx.x / WAVE;
   const int lane = lane_id();
   const int64_t t = int64_t(blockIdx.x) * 4 + wave;
   if (t >= p.tokens) return;
-  for (int e = lane; e < p.n_experts; e += WAVE) lds_l[wave][e] = p.logits[t * p.n_experts + e];
+  float l[RT_EPL], b[RT_EPL];
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int e = lane + WAVE * j;
+    if (e < p.n_experts) {
+      l[j] = p.logits[t * p.n_experts + e];
+      b[j] = p.e_bias[e];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int e = lane + WAVE * j;
+    if (e < p.n_experts) {
+      lds_l[wave][e] = l[j];
+      lds_b[wave][e] = b[j];
+    }
+  }
   wave_lds_sync();
-  select_one(p, lds_l[wave], t, scr[wave], p.e_bias);
+  select_one(p, lds_l[wave], t, scr[wave], lds_b[wave]);
 }
 
 }  // namespace
+
+hipError_t launch_route_logits_waves(const RouteArgs& p, int kind, hipStream_t stream, Timing t) {
+  dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK * (p.n_experts / 16)));
+  if (kind == K_F32) return launch_k(route_logits_kernel<K_F32>, grid, dim3(WAVE), stream, t, p);
+  return launch_k(route_logits_kernel<K_BF16>, grid, dim3(WAVE), stream, t, p);
+}
 
 hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stream, Timing t) {
   const Timing first{t.start, nullptr};
@@ -127,11 +152,7 @@ hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stre
     return launch_k(route_kernel<K_BF16>, grid, block, stream, t, p);
   }
   if (mode == ROUTE_WAVES) {
-    dim3 grid(static_cast<unsigned>((p.tokens + RT_TOK - 1) / RT_TOK * (p.n_experts / 16)));
-    if (kind == K_F32)
-      e = launch_k(route_logits_kernel<K_F32>, grid, dim3(WAVE), stream, first, p);
-    else
-      e = launch_k(route_logits_kernel<K_BF16>, grid, dim3(WAVE), stream, first, p);
+    e = launch_route_logits_waves(p, kind, stream, first);
   } else {  // ROUTE_GEMM: the logits as a dense GEMM
     GemmArgs g{};
     GemmProblem& q = g.prob[0];

@@ -23,6 +23,8 @@ ALL_GROUPS = Workload("all-groups-T33", 33, 128, 64, 8, 8, 8, 128, 64, "bf16", "
 WHOLE_GROUP = Workload("k-fills-group-T50", 50, 128, 32, 4, 1, 8, 64, 0, "bf16", "bf16", seed=25)
 BIG_ROWS = Workload("many-rows-T600", 600, 128, 16, 2, 1, 2, 128, 128, "bf16", "bf16", seed=26)
 SINGLE = dataclasses.replace(WORKLOADS["decode-bf16-T32"], name="decode-bf16-T1", tokens=1)
+# a few tokens: selection and permute share one launch in moe_forward
+FEW_FP4 = dataclasses.replace(WORKLOADS["decode-fp4-T32"], name="decode-fp4-T3", tokens=3)
 # Hundreds of rows per expert: the 256 x 256 tile kernels (I = 320 leaves a
 # partial N tile; d = 64 gives a K loop shorter than the DMA ring).
 BIG_GROUPS_BF16 = Workload("big-groups-bf16-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16",
@@ -45,7 +47,8 @@ FP4_MAX_K = Workload("fp4-max-k-T20", 20, 8192, 16, 4, 1, 2, 256, 0, "bf16", "fp
 
 SMALL = [WORKLOADS["tiny-f32-T64"], RAGGED_BF16, RAGGED_FP8, PLAIN_TOPK, ALL_GROUPS, WHOLE_GROUP,
          BIG_ROWS, WORKLOADS["decode-bf16-T32"], SINGLE, BIG_GROUPS_BF16, BIG_GROUPS_FP8, SHORT_K,
-         RAGGED_FP4, FP4_BF16_SHARED, FP4_MANY_ROWS, WORKLOADS["decode-fp4-T32"], FP4_MAX_K]
+         RAGGED_FP4, FP4_BF16_SHARED, FP4_MANY_ROWS, WORKLOADS["decode-fp4-T32"], FP4_MAX_K,
+         FEW_FP4]
 
 
 @pytest.fixture(scope="module", autouse=True)
