@@ -221,8 +221,10 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
  * hipEventElapsedTime of the pair is the stage's device time.  Stages that do
  * not run for the configuration leave their events untouched. */
 enum {
-  MOE_T_ROUTE = 0,        /* router + grouped top-k                       */
-  MOE_T_PERMUTE = 1,      /* histogram, scan, stable placement            */
+  MOE_T_ROUTE = 0,        /* router + grouped top-k (up to 4 tokens: the
+                             logits only)                                  */
+  MOE_T_PERMUTE = 1,      /* histogram, scan, stable placement (up to 4
+                             tokens: with the grouped top-k, one launch)   */
   MOE_T_QUANT_X = 2,      /* fp8 experts: per-token e4m3 quantisation of x */
   MOE_T_ROUTED_UP = 3,    /* routed up GEMM + relu^2                      */
   MOE_T_QUANT_H = 4,      /* fp8 experts: per-row e4m3 quantisation of h  */
