@@ -354,7 +354,6 @@ class MoELayer:
                        expert_counts=self.expert_counts, stage_events=stage_events,
                        ws_up_scale=t.get("ws_up_bscale"), ws_down_scale=t.get("ws_down_bscale"))
 
-
     def block(self, x, out=None, stage_events=None):
         """out = x + layer(RMSNorm(x)) (moe_block_forward); ``out`` may be ``x``."""
         T = x.shape[0]

@@ -401,3 +401,25 @@ def test_decode_rows_past_32_bit_offsets():
     assert_close_rms(to_f64(big)[pick], ref, "rows past 2 GiB")
     del a
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl", [RAGGED_BF16, RAGGED_FP8, RAGGED_FP4], ids=lambda w: w.name)
+def test_concurrent_calls_on_two_streams(wl):
+    # the library keeps no state between calls: two layers with workspaces of
+    # their own, enqueued on two streams at once, give the bits of sequential calls
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    la, lb = binding.MoELayer(wl, inp), binding.MoELayer(wl, inp)
+    xa, xb = t["x"], t["x"][:40].contiguous()
+    ref_a, ref_b = la(xa).clone(), lb(xb).clone()
+    torch.cuda.synchronize()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(4):
+        sa.wait_stream(torch.cuda.current_stream())
+        sb.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(sa):
+            ya = la(xa)
+        with torch.cuda.stream(sb):
+            yb = lb(xb)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(ya), _bits(ref_a)) and torch.equal(_bits(yb), _bits(ref_b))
