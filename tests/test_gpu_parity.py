@@ -271,8 +271,14 @@ def test_identical_experts_reduce_to_one_dense_mlp():
     assert_close_rms(to_f64(y), 2.5 * ffn + sh, "identical experts")
 
 
+# 6000 routing slots: the multi-workgroup permute, and 256-row tiles of the ring kernel
+MANY_CHUNKS = Workload("many-chunks-T3000", 3000, 128, 16, 2, 1, 2, 64, 64, "bf16", "bf16",
+                       seed=35)
+
+
 @pytest.mark.parametrize("wl", [WORKLOADS["decode-bf16-T32"], RAGGED_FP8,
-                                WORKLOADS["decode-fp4-T32"]], ids=lambda w: w.name)
+                                WORKLOADS["decode-fp4-T32"], SINGLE, MANY_CHUNKS],
+                         ids=lambda w: w.name)
 def test_graph_replays_match_eager(wl):
     # every replay is checked, with eager work and synchronisations between them
     inp = make_inputs(wl)
