@@ -23,7 +23,8 @@
 //    a double buffer in LDS, the next stage's loads issued before the current
 //    stage's MFMAs;
 //  * hundreds of rows per expert: 256 x 256 tiles, gemm_ring_kernel (K in
-//    64-byte slices fetched straight into a 4-stage LDS ring);
+//    64-byte slices fetched straight into a 4-stage LDS ring; fp8 keeps the
+//    weight rows two 128-byte steps ahead, the activation rows one);
 //  * the router's logits (a dense GEMM against the small gate matrix):
 //    gemm_stream_kernel, thin tiles over a DMA ring;
 //  * MXFP4 weights: gemm_fp4_kernel (16- or 64-row tiles).
@@ -393,9 +394,11 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   static_assert(DMA_PER_WAVE % QUARTERS == 0 && FN % QUARTERS == 0, "quarter split");
   // (a fifth bf16 slot, 160 KB in all, measured 2-3% slower)
   static_assert(KIND == K_BF16 ? (RING == 4 || RING == 5) : RING == 4, "ring depth");
-  // the ring, then (fp8) the tile's row and column scales
-  constexpr int SCALE_BYTES = KIND == K_FP8 ? 4 * (RG_BM + RG_BN) : 0;
-  __shared__ __attribute__((aligned(1024))) char ring[RING * RG_STAGE + SCALE_BYTES];
+  // the ring: RING stages (bf16); for fp8 two activation slots and three
+  // weight slots of two stages each, 160 KB
+  constexpr int RING_BYTES = KIND == K_FP8 ? 5 * RG_STAGE : RING * RG_STAGE;
+  static_assert(KIND != K_FP8 || NW * WAVE == RG_BM + RG_BN, "one scale per thread");
+  __shared__ __attribute__((aligned(1024))) char ring[RING_BYTES];
 
   Tile t;
   const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
@@ -442,19 +445,20 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     for (int q = 0; q < DMA_PER_WAVE; ++q) dma_one(q, s, buf);
   };
 
-  // fp8: the tile's row scales (activation rows) and column scales (weight
-  // rows), staged once in LDS for the epilogue; the K loop's first barrier
-  // makes them visible.
-  float* sc_row = reinterpret_cast<float*>(ring + RING * RG_STAGE);
+  // fp8: thread i holds scale i of the tile (the activation rows' scales,
+  // then the weight rows'); they move into the ring once the K loop has
+  // freed it, for the epilogue.
+  float* sc_row = reinterpret_cast<float*>(ring);
   float* sc_col = sc_row + RG_BM;
+  float my_scale = 0.0f;
   if constexpr (KIND == K_FP8) {
     const int i = threadIdx.x;
     if (i < RG_BM) {
       const int64_t r = t.m0 + i;
-      sc_row[i] = r < t.gend ? p.a_scale[src_row(p, r)] : 0.0f;
-    } else if (i < RG_BM + RG_BN) {
+      my_scale = r < t.gend ? p.a_scale[src_row(p, r)] : 0.0f;
+    } else {
       const int n = t.n0 + i - RG_BM;
-      sc_col[i - RG_BM] = n < p.n ? p.w_scale[int64_t(t.g) * p.n + n] : 0.0f;
+      my_scale = n < p.n ? p.w_scale[int64_t(t.g) * p.n + n] : 0.0f;
     }
   }
 
@@ -566,24 +570,18 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
 
   // fp8: one MFMA K step (16x16x128) takes 128 bytes of each row, ring
   // stages 2u and 2u + 1; lane group g holds bytes [32 g, 32 g + 32), i.e.
-  // chunks 2 (g & 1) and 2 (g & 1) + 1 of stage 2u + (g >> 1).  Steps use the
-  // slot pairs {0, 1} and {2, 3} in turn: the pair of step u + 1 is fetched
-  // during step u.  A stage past the end of K (K / 64 odd) is zero-filled in
-  // LDS, so the last step adds exact zeros.
-  auto zero_fill = [&](char* buf) {
-#pragma unroll
-    for (int q = 0; q < DMA_PER_WAVE; ++q)
-      *reinterpret_cast<i32x4_t*>(buf + (wave + NW * q) * 1024 + lane * 16) = i32x4_t{0, 0, 0, 0};
-  };
-  auto fill = [&](int s, char* buf) {
-    if (s < nk)
-      dma(s, buf);
-    else
-      zero_fill(buf);
-  };
+  // chunks 2 (g & 1) and 2 (g & 1) + 1 of stage 2u + (g >> 1).  The
+  // activation rows (from L2) of step u sit in slot u % 2 of their own
+  // region, fetched one step ahead; the weight rows (from HBM) in slot u % 3
+  // of theirs, fetched two steps ahead.  Each slot holds the step's two
+  // stages.  A stage past the end of K (K / 64 odd) is zero-filled in LDS,
+  // so the last step adds exact zeros.
   auto k_loop_fp8 = [&](auto fmv_c, auto full_c) {
     constexpr int FMV = decltype(fmv_c)::value;
     constexpr bool FULL_N = decltype(full_c)::value;
+    constexpr int HALF = RG_ABYTES;  // one stage of one operand
+    char* const a_region = ring;             // 2 slots
+    char* const b_region = ring + 4 * HALF;  // 3 slots
     const int c0 = 2 * (lgrp & 1);
     const int o0 = lrow * RG_ROWB + ((c0 ^ rg_swizzle(lrow)) * 16);
     const int o1 = lrow * RG_ROWB + (((c0 + 1) ^ rg_swizzle(lrow)) * 16);
@@ -595,26 +593,58 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
       return r;
     };
-    const int nsteps = (nk + 1) / 2;
-    fill(0, ring);
-    fill(1, ring + RG_STAGE);
-    for (int u = 0; u < nsteps; ++u) {
-      // this wave's fills of stages 2u, 2u + 1 have landed and its reads of
-      // step u - 1 are done; after the barrier the same holds for all waves
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
-      block_sync_lds();
-      char* nxt = ring + ((u + 1) & 1) * 2 * RG_STAGE;
-      if (u + 1 < nsteps) {
-        fill(2 * u + 2, nxt);
-        fill(2 * u + 3, nxt + RG_STAGE);
+    // stage s of one operand: this wave's blocks q0 and q0 + 1 (block b of
+    // the stage lands at dst + 1 KB b)
+    auto fill_half = [&](int s, char* dst, int q0) {
+      if (s < nk) {
+        dma_one(q0, s, dst);
+        dma_one(q0 + 1, s, dst);
+      } else {
+#pragma unroll
+        for (int q = q0; q < q0 + 2; ++q)
+          *reinterpret_cast<i32x4_t*>(dst + (wave + NW * q) * 1024 + lane * 16) =
+              i32x4_t{0, 0, 0, 0};
       }
-      const char* cur = ring + (u & 1) * 2 * RG_STAGE + (lgrp >> 1) * RG_STAGE;
+    };
+    auto fill_a = [&](int u) {
+      char* a = a_region + (u & 1) * 2 * HALF;
+      fill_half(2 * u, a, 0);
+      fill_half(2 * u + 1, a + HALF, 0);
+    };
+    auto fill_b = [&](int u) {
+      char* b = b_region + (u % 3) * 2 * HALF - HALF;  // weight blocks are 16..31
+      fill_half(2 * u, b, 2);
+      fill_half(2 * u + 1, b + HALF, 2);
+    };
+    // this wave's weight fetches per step (blocks q = 2, 3 of both stages)
+    const int nb = 2 * (((dma_on >> 2) & 1) + ((dma_on >> 3) & 1));
+    const int nsteps = (nk + 1) / 2;
+    fill_a(0);
+    fill_b(0);
+    if (nsteps > 1) fill_b(1);
+    for (int u = 0; u < nsteps; ++u) {
+      // this wave's fetches of step u (issued before those of the weights of
+      // step u + 1) have landed and its reads of step u - 1 are done; after
+      // the barrier the same holds for all waves.  The weights of step u + 1
+      // may still fly when both their stages are fetches.
+      const bool relaxed = 2 * u + 3 < nk;
+      if (relaxed && nb == 4)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
+      else if (relaxed && nb == 2)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 0));
+      else
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+      block_sync_lds();
+      if (u + 1 < nsteps) fill_a(u + 1);
+      if (u + 2 < nsteps) fill_b(u + 2);
+      const char* ca = a_region + (u & 1) * 2 * HALF + (lgrp >> 1) * HALF;
+      const char* cb = b_region + (u % 3) * 2 * HALF + (lgrp >> 1) * HALF;
       i32x8_t af[FM], bf[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        if (FULL_N || j < fn_valid) bf[j] = frag(cur + RG_ABYTES + (wn + WN * j) * 1024);
+        if (FULL_N || j < fn_valid) bf[j] = frag(cb + (wn + WN * j) * 1024);
 #pragma unroll
-      for (int i = 0; i < FMV; ++i) af[i] = frag(cur + (wm + WM * i) * 1024);
+      for (int i = 0; i < FMV; ++i) af[i] = frag(ca + (wm + WM * i) * 1024);
 #pragma unroll
       for (int i = 0; i < FMV; ++i)
 #pragma unroll
@@ -644,10 +674,14 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     else
       with_rows(loop, std::false_type{});
   };
-  if constexpr (KIND == K_FP8)
+  if constexpr (KIND == K_FP8) {
     run(k_loop_fp8);
-  else
+    __syncthreads();  // every wave is past its last fragment read
+    sc_row[threadIdx.x] = my_scale;
+    __syncthreads();
+  } else {
     run(k_loop);
+  }
 
   // Epilogue: the same arithmetic as store_block, fp8 scales from LDS.  The
   // MFMAs take the weight fragment as their first operand, so a lane holds
