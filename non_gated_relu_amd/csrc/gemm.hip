@@ -572,8 +572,9 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   // stages 2u and 2u + 1; lane group g holds bytes [32 g, 32 g + 32), i.e.
   // chunks 2 (g & 1) and 2 (g & 1) + 1 of stage 2u + (g >> 1).  The
   // activation rows (from L2) of step u sit in slot u % 2 of their own
-  // region, fetched one step ahead; the weight rows (from HBM) in slot u % 3
-  // of theirs, fetched two steps ahead.  Each slot holds the step's two
+  // region, fetched one step ahead at the top of the step; the weight rows
+  // (from HBM) in slot u % 3 of theirs, fetched two steps ahead halfway
+  // through the step's MFMAs.  Each slot holds the step's two
   // stages.  A stage past the end of K (K / 64 odd) is zero-filled in LDS,
   // so the last step adds exact zeros.
   auto k_loop_fp8 = [&](auto fmv_c, auto full_c) {
@@ -636,7 +637,6 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
       block_sync_lds();
       if (u + 1 < nsteps) fill_a(u + 1);
-      if (u + 2 < nsteps) fill_b(u + 2);
       const char* ca = a_region + (u & 1) * 2 * HALF + (lgrp >> 1) * HALF;
       const char* cb = b_region + (u % 3) * 2 * HALF + (lgrp >> 1) * HALF;
       i32x8_t af[FM], bf[FN];
@@ -646,7 +646,17 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
 #pragma unroll
       for (int i = 0; i < FMV; ++i) af[i] = frag(ca + (wm + WM * i) * 1024);
 #pragma unroll
-      for (int i = 0; i < FMV; ++i)
+      for (int i = 0; i < FMV / 2; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
+      // the weights of step u + 2 between the two halves of the MFMAs: the
+      // fragment reads go first, and the fetches have two steps to land
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + 2 < nsteps) fill_b(u + 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = FMV / 2; i < FMV; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
