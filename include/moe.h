@@ -38,6 +38,18 @@
  *  - Inputs must be finite; routing of NaN/Inf scores is unspecified.
  *  - Results are deterministic: no floating-point atomics, fixed reduction
  *    orders, so reruns are bitwise identical.
+ *
+ * Deliberate departures from a plain statement of the five calls
+ *  - moe_permute takes no row-scale output for its gathered rows: with fp8
+ *    experts the activation rows are quantised inside moe_expert_ffn (one
+ *    scale per row, before the up GEMM), not at the permute, and the permuted
+ *    rows are gathered by the GEMM while loading rather than materialised.
+ *  - moe_expert_ffn takes the weights' type (w_dtype) and a row-index divisor
+ *    (index_div): one call then serves the routed experts (rows gathered
+ *    through the sorted slots, slot / k = token) and the shared expert (the
+ *    rows as they are), in bf16, fp32, fp8 or fp4 weights.
+ *  - moe_forward takes the shared expert's block scales (ws_up_scale,
+ *    ws_down_scale) for 4-bit shared-expert weights.
  */
 #ifndef NGR_MOE_H
 #define NGR_MOE_H
@@ -114,7 +126,11 @@ moe_status moe_route(const moe_config* cfg, int64_t tokens, const void* x, const
                      const float* e_bias, int32_t* topk_idx, float* topk_w, void* workspace,
                      size_t workspace_bytes, void* stream);
 
-/* Stable grouping of the tokens*k routing slots (slot s = t*k + j) by expert:
+/* Stable grouping of the tokens*k routing slots (slot s = t*k + j) by expert.
+ * The experts are applied as one stacked weight tensor per projection to the
+ * rows routed to them (exo commit "Add support for Nemotron sharding": the
+ * SwitchMLP typing stub, fc1 and fc2 called as switch_mlp(x, indices)); this
+ * call produces that grouping, so each expert's rows are contiguous:
  *   expert_counts  [E]        int32 out
  *   expert_offsets [E+1]      int32 out, exclusive prefix sum of the counts
  *   sorted_slot    [tokens*k] int32 out, slot at each sorted position; within
@@ -133,7 +149,13 @@ moe_status moe_expert_ffn_workspace_size(const moe_config* cfg, int32_t n_mats, 
                                          int32_t w_dtype, int64_t a_rows, int64_t rows,
                                          size_t* bytes);
 
-/* Grouped non-gated expert MLPs: for each matrix pair m and each problem row r
+/* Grouped non-gated expert MLPs.  An expert is up_proj -> relu^2 -> down_proj
+ * with no gate projection (vllm.cpp PR "spec(MODEL-TEXT-nemotron-h)", its
+ * description of the expert MLP) and no bias (auto-round PR "feat: support
+ * Nemotron-H / Nemotron-Cascade-2", quantisation log: Linear(2688 -> 1856)
+ * and Linear(1856 -> 2688) with bias=False); the shared expert is the same
+ * MLP at its own width (exo commit, NemotronHMLP stub).  For each matrix pair
+ * m and each problem row r
  * in [row_offsets[m], row_offsets[m+1]):
  *     out[r] = Wdown[m] relu(Wup[m] a[src(r)])^2,  src(r) = row_index[r] / index_div
  *                                                  (or r when row_index is NULL)

@@ -11,6 +11,12 @@ from non_gated_relu_amd import binding
 # fp32 accumulation): max-abs 2e-2 and mean-abs 2e-3.
 MAX_TOL = 2e-2
 MEAN_TOL = 2e-3
+# Rows that may need the fp8 flip allowance (beyond the plain max gate): at
+# most this fraction of the rows checked, and at least one.  Flips need an
+# element of h within 1e-4 relative of an e4m3 midpoint and then a large
+# enough down-projection weight; 2 of 1200 rows were seen, so a regression
+# that pushes many rows off by a code step fails here.
+FLIP_ROW_FRAC = 0.01
 # Routing weights: fp32-accumulated logits differ from fp64 by up to a few
 # 1e-6 at d = 2688; ds/s = (1 - s) dl, and w = s / sum(s) doubles that at
 # most, plus a few fp32 ulps of the normalisation: below 1e-5 relative.
@@ -34,7 +40,8 @@ def assert_close_rms(got, ref, what: str, max_tol=MAX_TOL, mean_tol=MEAN_TOL, R=
     """max-abs <= max_tol R and mean-abs <= mean_tol R, R = RMS of ref.
 
     row_allow: optional per-row extra absolute allowance of the max-abs gate
-    (fp8 rounding flips, see fp8_flips); the mean gate is unchanged."""
+    (fp8 rounding flips, see fp8_flips); the mean gate is unchanged, and at
+    most FLIP_ROW_FRAC of the rows (at least one) may use the allowance."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     R = rms(ref) if R is None else R
@@ -48,8 +55,13 @@ def assert_close_rms(got, ref, what: str, max_tol=MAX_TOL, mean_tol=MEAN_TOL, R=
     row_err = err.reshape(err.shape[0], -1).max(axis=1)
     allow = np.asarray(row_allow, np.float64)
     over = row_err > max_tol * R
+    cap = max(1, int(FLIP_ROW_FRAC * over.size))
+    worst = float((allow[over] / R).max()) if over.any() else 0.0
     print(f"{what}: {int((allow > 0).sum())} of {allow.size} rows have e4m3 values near a "
-          f"rounding midpoint, {int(over.sum())} of them beyond the plain gate", flush=True)
+          f"rounding midpoint, {int(over.sum())} rows beyond the plain gate (cap {cap}), "
+          f"largest allowance used {worst:.3e} R", flush=True)
+    assert over.sum() <= cap, (f"{what}: {int(over.sum())} rows beyond the plain max gate, "
+                               f"more than the {cap} an fp8 rounding flip explains")
     bad = np.flatnonzero(row_err > max_tol * R + allow)
     assert bad.size == 0, (f"{what}: rows {bad[:8].tolist()} exceed max_tol R + allowance "
                            f"(err/R {(row_err[bad[:8]] / R).round(4).tolist()}, "

@@ -1,7 +1,9 @@
 """GPU parity at the full Nemotron-H sizes, in the launch configuration the
 benchmark times (one moe_forward per step): routing and per-expert counts for
-every token, the output on a seeded sample of tokens the oracle computes one
-by one."""
+every token, the layer output on 1024 tokens the oracle computes one by one,
+and the routed expert MLP rows of moe_expert_ffn on at least 4096 rows per
+workload (the first rows, both ends of every active expert's rows, the last
+partial 256-row tile of every expert, and seeded random rows)."""
 
 import numpy as np
 import pytest
@@ -38,11 +40,37 @@ def _inputs(name):
     return inp
 
 
-def _sample(T, n=48, seed=0):
+TOKENS_CHECKED = 1024
+ROWS_CHECKED = 4096
+
+
+def _sample(T, n=TOKENS_CHECKED, seed=0):
+    """n distinct tokens: the first 3n/4, seeded random ones, and the last."""
     rng = np.random.default_rng(seed)
-    s = np.concatenate([np.arange(min(16, T)), rng.choice(T, size=min(n, T), replace=False),
-                        [T - 1]])
-    return np.unique(s)
+    first = np.arange(min(3 * n // 4, T))
+    rest = np.setdiff1d(np.arange(T), np.append(first, T - 1))
+    extra = rng.choice(rest, size=min(n - first.size - 1, rest.size), replace=False)
+    return np.unique(np.concatenate([first, extra, [T - 1]]))
+
+
+def _row_sample(offsets, n=ROWS_CHECKED, tile=256, seed=1):
+    """Sorted routed-row positions to check: the first 512, the first two and
+    last two rows of every active expert, up to 16 rows of every expert's last
+    (partial) tile of `tile` rows, then seeded random rows up to n."""
+    S = int(offsets[-1])
+    pick = [np.arange(min(512, S))]
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi <= lo:
+            continue
+        pick.append(np.array([lo, min(lo + 1, hi - 1), max(hi - 2, lo), hi - 1]))
+        last = lo + (hi - lo - 1) // tile * tile  # first row of the last tile
+        pick.append(np.linspace(last, hi - 1, num=min(16, hi - last)).astype(np.int64))
+    rows = np.unique(np.concatenate(pick))
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(S), rows)
+    extra = rng.choice(rest, size=min(max(n - rows.size, 0), rest.size), replace=False)
+    return np.unique(np.concatenate([rows, extra]))
 
 
 @pytest.mark.parametrize("name", ["prefill-bf16-T4096", "skew-bf16-T16384", "fp8-T8192"])
@@ -90,3 +118,41 @@ def test_full_size_layer(name):
     bad = (yc.view(torch.int16) != y.view(torch.int16)).any(dim=1).nonzero().flatten()
     assert bad.numel() == 0, f"{name}: {bad.numel()} rows differ from the chunked run, " \
                              f"first {bad[:8].tolist()}"
+
+
+@pytest.mark.parametrize("name", ["prefill-bf16-T4096", "skew-bf16-T16384", "fp8-T8192"])
+def test_full_size_expert_rows(name):
+    """moe_expert_ffn over all routed rows of the workload (the routed problem
+    moe_forward runs, in its tile shape) against the oracle's per-row expert
+    MLP on at least ROWS_CHECKED rows."""
+    print(f"case {name} expert rows", flush=True)
+    wl = WORKLOADS[name]
+    inp = _inputs(name)
+    t = upload({k: v for k, v in inp.items() if k != "norm_w"}, wl)
+    cfg = binding.config_from(wl)
+    idx, _, _ = oracle.route(wl, inp["x"], inp["w_gate"], inp["e_bias"])
+    counts, offsets, sorted_slot, _ = oracle.permute(idx, wl.n_experts)
+    k = wl.top_k
+    off_d = torch.from_numpy(offsets).cuda()
+    ss_d = torch.from_numpy(sorted_slot).cuda()
+    S = int(offsets[-1])
+    y_perm = binding.expert_ffn(cfg, t["w_up"], t["w_down"], t["x"], off_d, S, row_index=ss_d,
+                                index_div=k, w_dtype=wl.expert_dtype,
+                                w_up_scale=t.get("w_up_scale"), w_down_scale=t.get("w_down_scale"))
+    torch.cuda.synchronize()
+    pos = _row_sample(offsets)
+    assert pos.size >= ROWS_CHECKED
+    rows = sorted_slot[pos] // k
+    mats = np.repeat(np.arange(wl.n_experts), counts)[pos]
+    active = np.flatnonzero(counts)
+    assert np.isin(active, mats).all(), "every active expert is checked"
+    ref = oracle.ffn_rows(inp["x"], wl.act_dtype, rows, mats, inp["w_up"], inp["w_down"],
+                          wl.expert_dtype, inp.get("w_up_scale"), inp.get("w_down_scale"),
+                          quant_a=wl.expert_dtype == "fp8")
+    allow = None
+    if wl.expert_dtype == "fp8":
+        allow = fp8_flips.row_allowance(inp["x"], rows, mats, inp["w_up"], inp["w_up_scale"],
+                                        inp["w_down"], inp["w_down_scale"])
+    got = to_f64(y_perm[torch.from_numpy(pos).cuda()])
+    print(f"{name}: {pos.size} routed rows over {active.size} experts", flush=True)
+    assert_close_rms(got, ref, f"{name} expert rows", row_allow=allow)
