@@ -235,6 +235,29 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
                        int32_t* expert_counts, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches and results, with the workspace taken from a static device
+ * array of MOE_STATIC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  The call allocates nothing; its first
+ * call on a device resolves that device's copy of the array (the current
+ * device: `stream` must belong to it).
+ *   Sizes: calls whose moe_workspace_size(cfg, tokens) exceeds
+ *   MOE_STATIC_SCRATCH_BYTES return MOE_ERR_WORKSPACE and enqueue nothing
+ *   (bf16 layers of the Nemotron-H shape: up to about 600 tokens).
+ *   Sharing: every call on one GPU uses the same array and leaves its
+ *   contents there; calls that overlap in time on one GPU (other streams,
+ *   other threads) race and give undefined results.  Calls on one stream run
+ *   in order and are safe.  Nothing in it needs clearing between calls. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_static(const moe_config* cfg, int64_t tokens, const void* x,
+                              const void* w_gate, const float* e_bias, const void* w_up,
+                              const void* w_up_scale, const void* w_down,
+                              const void* w_down_scale, const void* ws_up,
+                              const void* ws_up_scale, const void* ws_down,
+                              const void* ws_down_scale, void* y, int32_t* topk_idx,
+                              float* topk_w, int32_t* expert_counts, void* stream);
+
 /* Measurement variant of moe_forward: the same launches and results.  When
  * `stage_events` is not NULL it holds 2 * MOE_T_SLOTS hipEvent_t created by
  * the caller (entries may be NULL); the kernels of stage i are launched with

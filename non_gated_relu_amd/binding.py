@@ -70,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.argtypes = [_cfgp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [_vp]
+        L.moe_forward_static.argtypes = [_cfgp, _i64] + [_vp] * 16
         L.moe_rmsnorm.argtypes = [_cfgp, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]
         L.moe_block_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_block_forward.argtypes = ([_cfgp, _i64, _vp, _vp, ctypes.c_float] +
@@ -78,7 +79,7 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_rows.argtypes = [_i32, _i64, _i32, _vp, _vp, _vp, _vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
-                     "moe_forward", "moe_forward_timed", "moe_rmsnorm",
+                     "moe_forward", "moe_forward_timed", "moe_forward_static", "moe_rmsnorm",
                      "moe_block_workspace_size", "moe_block_forward",
                      "moe_block_forward_timed", "moe_quantize_rows"):
             getattr(L, name).restype = ctypes.c_int
@@ -236,6 +237,26 @@ def forward(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down, w_u
     else:
         _check(lib().moe_forward_timed(*args, stage_events.array), "moe_forward_timed")
     return y
+
+
+def forward_static(cfg: MoeConfig, x, w_gate, e_bias, w_up, w_down, ws_up, ws_down,
+                   w_up_scale=None, w_down_scale=None, y=None, topk_idx=None, topk_w=None,
+                   expert_counts=None, ws_up_scale=None, ws_down_scale=None):
+    """moe_forward_static: moe_forward with the library's static device scratch
+    as its workspace (nothing is allocated by the library; ``y`` is allocated
+    here only when not given)."""
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, cfg.hidden), dtype=x.dtype, device=x.device)
+    _check(lib().moe_forward_static(ctypes.byref(cfg), T, _p(x), _p(w_gate), _p(e_bias),
+                                    _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale),
+                                    _p(ws_up), _p(ws_up_scale), _p(ws_down), _p(ws_down_scale),
+                                    _p(y), _p(topk_idx), _p(topk_w), _p(expert_counts),
+                                    _stream()), "moe_forward_static")
+    return y
+
+
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES
 
 
 def block_workspace_size(cfg: MoeConfig, tokens: int) -> int:

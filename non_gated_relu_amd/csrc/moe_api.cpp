@@ -19,6 +19,7 @@
 //   routed experts it gets its own two bf16 launches.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "moe.h"
 #include "internal.hpp"
@@ -478,11 +479,43 @@ moe_status run_forward(const moe_config* cfg, int64_t tokens, const void* x,
   return hip_status(launch_combine(p, c.act_dtype == MOE_BF16, s, slot(ev, MOE_T_COMBINE)));
 }
 
+// ----------------------------------------------- static scratch (no allocation)
+//
+// moe_forward_static's workspace: one file-scope device array, which every
+// GPU the library runs on holds (at its own address) until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so
+// the device address comes from hipGetSymbolAddress, once per device with
+// that device current, and only that address is ever handed to kernels.
+// Nothing in the forward's workspace needs to start at zero (every buffer is
+// written before it is read), so the array is never cleared.
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(MOE_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// The device address of the current device's scratch (resolved on the first
+// call on that device).
+moe_status static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 4; }
+int32_t moe_abi_version(void) { return 5; }
 
 const char* moe_status_string(moe_status st) {
   switch (st) {
@@ -659,6 +692,29 @@ moe_status moe_forward(const moe_config* cfg, int64_t tokens, const void* x, con
   return moe_forward_timed(cfg, tokens, x, w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
                            ws_up, ws_up_scale, ws_down, ws_down_scale, y, topk_idx, topk_w,
                            expert_counts, workspace, workspace_bytes, stream, nullptr);
+}
+
+moe_status moe_forward_static(const moe_config* cfg, int64_t tokens, const void* x,
+                              const void* w_gate, const float* e_bias, const void* w_up,
+                              const void* w_up_scale, const void* w_down,
+                              const void* w_down_scale, const void* ws_up,
+                              const void* ws_up_scale, const void* ws_down,
+                              const void* ws_down_scale, void* y, int32_t* topk_idx,
+                              float* topk_w, int32_t* expert_counts, void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
+  if (tokens == 0) return MOE_OK;
+  // sizes beyond the scratch are refused before anything is resolved or enqueued
+  Carver measure(nullptr);
+  carve_forward(measure, *cfg, tokens);
+  if (measure.used > STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = static_scratch(&ws)) != MOE_OK) return st;
+  const LayerWeights w{w_gate, e_bias, w_up, w_up_scale, w_down, w_down_scale,
+                       ws_up, ws_up_scale, ws_down, ws_down_scale};
+  return run_forward(cfg, tokens, x, nullptr, 0.0f, w, y, topk_idx, topk_w, expert_counts, ws,
+                     STATIC_SCRATCH_BYTES, stream, nullptr);
 }
 
 moe_status moe_quantize_rows(int32_t in_dtype, int64_t rows, int32_t cols, const void* in,

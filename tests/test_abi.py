@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
-    assert binding.lib().moe_abi_version() == 4
+    assert binding.lib().moe_abi_version() == 5
 
 
 def _cfg(**kw):
@@ -107,6 +107,21 @@ def test_zero_tokens_enqueue_nothing():
     assert L.moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, 0, None) == MOE_OK
     assert L.moe_forward(ctypes.byref(c), 0, *([None] * 16), 0, None) == MOE_OK
     assert L.moe_combine(ctypes.byref(c), 0, None, None, None, None, None, None) == MOE_OK
+
+
+def test_static_forward_refuses_sizes_beyond_its_scratch():
+    """moe_forward_static checks its size against the static scratch on the
+    host, before it resolves the scratch or enqueues anything."""
+    L = binding.lib()
+    c = _cfg()
+    assert L.moe_forward_static(ctypes.byref(c), 0, *([None] * 16)) == MOE_OK
+    big = 1
+    while _ws(c, big)[1] <= binding.STATIC_SCRATCH_BYTES:
+        big *= 2
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.moe_forward_static(ctypes.byref(c), big, *([fake] * 16)) == MOE_ERR_WORKSPACE
+    # the header's figure: a Nemotron-H-shaped bf16 layer fits up to about 600 tokens
+    assert _ws(c, 512)[1] <= binding.STATIC_SCRATCH_BYTES < _ws(c, 700)[1]
 
 
 def test_null_and_misaligned_pointers_are_refused():
