@@ -61,19 +61,20 @@ def mfma_dtype(dt):
     return "bf16" if dt == "fp4" else dt
 
 
-def stage_work(wl, active: int):
-    """Algorithmic bytes and flops of each stage's launch(es) for one step.
+def stage_work(wl, active: int, stages):
+    """Algorithmic bytes and flops of each stage's launch(es) for one step,
+    for the stages the library runs (binding.stages_of).
 
     ``bytes`` counts only what the method itself must move through the
     launch: the weights of the active experts (one unit = one expert
     projection of I*d elements with its scales: fp32 per row for fp8, E8M0
-    per 32 elements for fp4), the shared expert's weights when they ride in
-    the launch, the layer input x read by the up projections, and the layer
-    output y written by the combine.  Traffic that exists only because the
-    layer is split into launches (h written and read back, the fp32 per-slot
-    rows written by the down projection and read by the combine, the shared
-    expert's output, the routing indices) is ``implementation_bytes``,
-    reported beside it and never credited.
+    per 32 elements for fp4), the shared expert's weights in the launches
+    that run it, the layer input x read by the up projections, and the layer
+    output y written by whichever launch combines.  Traffic that exists only
+    because the layer is split into launches (h written and read back, the
+    fp32 per-slot rows written by the down projection and read by the
+    combine, the shared expert's fp32 rows, the routing indices) is
+    ``implementation_bytes``, reported beside it and never credited.
     """
     T, d, E, k, I, Is = wl.tokens, wl.hidden, wl.n_experts, wl.top_k, wl.inter, wl.shared_inter
     S = T * k
@@ -84,6 +85,10 @@ def stage_work(wl, active: int):
     h_out = 4 if fp8 or edt == "f32" else 2  # h as written by the up GEMM (bf16 for bf16, fp4)
     h_in = 1 if fp8 else h_out
     up_u, dn_u = wbytes(edt, I, d), wbytes(edt, d, I)
+    combined = "combine" not in stages   # the shared down projection combines
+    block = bool(getattr(wl, "block", False))
+    y_bytes = T * d * ae * (2 if block else 1)  # y written (+ the residual x read)
+    comb_impl = S * d * 4 + S * 8          # slot rows and routing weights read
     w = {
         "route": dict(bytes=T * d * ae + E * d * ae + E * 4, flops=2 * T * d * E,
                       implementation_bytes=S * 8, dtype=wl.act_dtype),
@@ -97,33 +102,36 @@ def stage_work(wl, active: int):
     if Is:
         sh_h = 4 if sdt == "f32" else 2
         su, sd = wbytes(sdt, Is, d), wbytes(sdt, d, Is)
-        if edt == sdt:
-            # the shared expert runs inside the routed launches as one more
-            # group; x is already counted by the routed rows of the up launch
-            for st, wb, fl, imp in (("routed_up", su, 2 * T * d * Is, T * Is * sh_h),
-                                    ("routed_down", sd, 2 * T * Is * d,
-                                     T * Is * sh_h + T * d * 4)):
-                w[st]["bytes"] += wb
-                w[st]["flops"] += fl
-                w[st]["implementation_bytes"] += imp
-                w[st]["shared_weight_bytes"] = wb
-        else:
+        sh_out = 0 if combined else T * d * 4      # the shared rows, unless combined
+        shared_down = dict(bytes=sd + (y_bytes if combined else 0), flops=2 * T * Is * d,
+                           implementation_bytes=T * Is * sh_h + sh_out +
+                           (comb_impl if combined else 0),
+                           dtype=mfma_dtype(sdt), unit_bytes=sd, units=1)
+        if "shared_up" in stages:
             w["shared_up"] = dict(bytes=su + T * d * ae, flops=2 * T * d * Is,
                                   implementation_bytes=T * Is * sh_h, dtype=mfma_dtype(sdt),
                                   unit_bytes=su, units=1)
-            w["shared_down"] = dict(bytes=sd, flops=2 * T * Is * d,
-                                    implementation_bytes=T * Is * sh_h + T * d * 4,
-                                    dtype=mfma_dtype(sdt), unit_bytes=sd, units=1)
-    w["combine"] = dict(bytes=T * d * ae, flops=0, dtype="f32",
-                        implementation_bytes=S * d * 4 + T * d * 4 * (1 if Is else 0) + S * 8)
+        else:  # one more group of the routed up launch (x is already counted)
+            w["routed_up"]["bytes"] += su
+            w["routed_up"]["flops"] += 2 * T * d * Is
+            w["routed_up"]["implementation_bytes"] += T * Is * sh_h
+            w["routed_up"]["shared_weight_bytes"] = su
+        if "shared_down" in stages:
+            w["shared_down"] = shared_down
+        else:  # one more group of the routed down launch
+            for key in ("bytes", "flops", "implementation_bytes"):
+                w["routed_down"][key] += shared_down[key]
+            w["routed_down"]["shared_weight_bytes"] = sd
+    if not combined:
+        w["combine"] = dict(bytes=y_bytes, flops=0, dtype="f32",
+                            implementation_bytes=comb_impl + (T * d * 4 if Is else 0))
     if fp8:
         w["quant_x"] = dict(bytes=0, flops=0, dtype="f32", implementation_bytes=T * d * (ae + 1) + T * 4)
         w["quant_h"] = dict(bytes=0, flops=0, dtype="f32", implementation_bytes=S * I * 5 + S * 4)
-    if getattr(wl, "block", False):
-        # the norm reads x and writes x_norm; combine also reads the residual x
+    if block:
+        # the norm reads x and writes x_norm
         w["norm"] = dict(bytes=T * d * ae + d * ae, flops=0, dtype="f32",
                          implementation_bytes=T * d * ae)
-        w["combine"]["bytes"] += T * d * ae
     return w
 
 
@@ -316,7 +324,7 @@ def main():
 
     counts = layer.expert_counts.cpu().numpy()
     active = int((counts > 0).sum())
-    work = stage_work(wl, active)
+    work = stage_work(wl, active, stages)
     ms_per_step = 1e3 * total_s / steps
     tokens_per_s = wl.tokens * steps / total_s
 

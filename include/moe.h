@@ -274,12 +274,21 @@ enum {
   MOE_T_ROUTED_UP = 3,    /* routed up GEMM + relu^2                      */
   MOE_T_QUANT_H = 4,      /* fp8 experts: per-row e4m3 quantisation of h  */
   MOE_T_ROUTED_DOWN = 5,  /* routed down GEMM                             */
-  MOE_T_SHARED_UP = 6,    /* shared-expert up GEMM + relu^2               */
-  MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM                      */
+  MOE_T_SHARED_UP = 6,    /* shared-expert up GEMM + relu^2 (its own
+                             launch when its weight type differs from the
+                             routed experts')                              */
+  MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM (its own launch when
+                             its weight type differs from the routed
+                             experts')                                     */
   MOE_T_COMBINE = 8,      /* weighted combine + output rounding           */
   MOE_T_NORM = 9,         /* block only: the RMSNorm before the layer     */
   MOE_T_SLOTS = 10
 };
+/* Which stages moe_forward runs for `tokens` tokens (host output): bit i of
+ * *mask is set when stage i of the enumeration above runs (0 for tokens ==
+ * 0).  moe_block_forward runs the same stages and MOE_T_NORM.  Host-only: no
+ * device is touched. */
+moe_status moe_forward_stage_mask(const moe_config* cfg, int64_t tokens, uint32_t* mask);
 moe_status moe_forward_timed(const moe_config* cfg, int64_t tokens, const void* x,
                              const void* w_gate, const float* e_bias, const void* w_up,
                              const void* w_up_scale, const void* w_down,

@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
                                   _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.moe_forward_timed.argtypes = L.moe_forward.argtypes + [_vp]
         L.moe_forward_static.argtypes = [_cfgp, _i64] + [_vp] * 16
+        L.moe_forward_stage_mask.argtypes = [_cfgp, _i64, ctypes.POINTER(ctypes.c_uint32)]
         L.moe_rmsnorm.argtypes = [_cfgp, _i64, _vp, _vp, ctypes.c_float, _vp, _vp]
         L.moe_block_workspace_size.argtypes = [_cfgp, _i64, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_block_forward.argtypes = ([_cfgp, _i64, _vp, _vp, ctypes.c_float] +
@@ -79,7 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_quantize_rows.argtypes = [_i32, _i64, _i32, _vp, _vp, _vp, _vp]
         for name in ("moe_workspace_size", "moe_route", "moe_permute",
                      "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
-                     "moe_forward", "moe_forward_timed", "moe_forward_static", "moe_rmsnorm",
+                     "moe_forward", "moe_forward_timed", "moe_forward_static",
+                     "moe_forward_stage_mask", "moe_rmsnorm",
                      "moe_block_workspace_size", "moe_block_forward",
                      "moe_block_forward_timed", "moe_quantize_rows"):
             getattr(L, name).restype = ctypes.c_int
@@ -326,18 +328,16 @@ class StageEvents:
             self.events[2 * STAGES.index(s) + 1]) for s in stages}
 
 
-def stages_of(wl, block: bool = False):
-    """The stages moe_forward (or, with ``block``, moe_block_forward) runs for a
-    workload (the shared expert has launches of its own only when its weight
-    type differs from the routed experts')."""
-    st = (["norm"] if block else []) + ["route", "permute"]
-    if wl.expert_dtype == "fp8":
-        st += ["quant_x", "routed_up", "quant_h", "routed_down"]
-    else:
-        st += ["routed_up", "routed_down"]
-    if wl.shared_inter and wl.expert_dtype != (getattr(wl, "shared_dtype", None) or wl.act_dtype):
-        st += ["shared_up", "shared_down"]
-    return st + ["combine"]
+def stages_of(wl, block: bool = False, tokens: int = None):
+    """The stages moe_forward (or, with ``block``, moe_block_forward) runs for
+    a workload, in launch order, as the library reports them
+    (moe_forward_stage_mask)."""
+    cfg = config_from(wl)
+    mask = ctypes.c_uint32()
+    _check(lib().moe_forward_stage_mask(ctypes.byref(cfg), tokens or wl.tokens,
+                                        ctypes.byref(mask)), "moe_forward_stage_mask")
+    st = ["norm"] if block else []
+    return st + [s for i, s in enumerate(STAGES) if s != "norm" and (mask.value >> i) & 1]
 
 
 class MoELayer:

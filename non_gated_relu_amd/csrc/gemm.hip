@@ -157,7 +157,8 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t, int bid
     const int b2 = bid - (pa.second_first ? n_second * pa.n_tiles2 : first * pa.n_tiles);
     const bool in_second = pa.second_first ? b2 < 0 : b2 >= 0;
     if (in_second) {
-      if (n_second <= 0) return false;  // (then n_tiles2 may be 0)
+      // (a launch without the second problem has n_tiles2 = 0)
+      if (n_second <= 0 || pa.n_tiles2 <= 0) return false;
       const int b = pa.second_first ? bid : b2;
       const int m2 = b / pa.n_tiles2;
       if (m2 >= n_second) return false;

@@ -381,6 +381,17 @@ struct LayerWeights {
   const void *ws_up, *ws_up_scale, *ws_down, *ws_down_scale;
 };
 
+// The stages moe_forward runs for a positive token count (bit i: stage i of
+// the MOE_T_* enumeration).
+uint32_t forward_stage_mask(const moe_config& c) {
+  uint32_t m = (1u << MOE_T_ROUTE) | (1u << MOE_T_PERMUTE) | (1u << MOE_T_ROUTED_UP) |
+               (1u << MOE_T_ROUTED_DOWN);
+  if (c.expert_dtype == MOE_FP8_E4M3) m |= (1u << MOE_T_QUANT_X) | (1u << MOE_T_QUANT_H);
+  const bool own_shared = c.shared_inter > 0 && c.expert_dtype != c.shared_dtype;
+  if (own_shared) m |= (1u << MOE_T_SHARED_UP) | (1u << MOE_T_SHARED_DOWN);
+  return m | (1u << MOE_T_COMBINE);
+}
+
 // Bytes of the block's normalised rows in the workspace.
 size_t norm_bytes(const moe_config& c, int64_t T) { return size_t(T) * c.hidden * esize(c.act_dtype); }
 
@@ -515,7 +526,7 @@ moe_status static_scratch(void** out) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return 5; }
+int32_t moe_abi_version(void) { return 6; }
 
 const char* moe_status_string(moe_status st) {
   switch (st) {
@@ -526,6 +537,15 @@ const char* moe_status_string(moe_status st) {
     case MOE_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
+}
+
+moe_status moe_forward_stage_mask(const moe_config* cfg, int64_t tokens, uint32_t* mask) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
+  if (!mask) return MOE_ERR_INVALID_ARG;
+  *mask = tokens > 0 ? forward_stage_mask(*cfg) : 0u;
+  return MOE_OK;
 }
 
 moe_status moe_workspace_size(const moe_config* cfg, int64_t tokens, size_t* bytes) {

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     L = ctypes.CDLL(binding.LIB_PATH)
     for n in _declared():
         assert hasattr(L, n), n
-    assert binding.lib().moe_abi_version() == 5
+    assert binding.lib().moe_abi_version() == 6
 
 
 def _cfg(**kw):
@@ -107,6 +107,29 @@ def test_zero_tokens_enqueue_nothing():
     assert L.moe_route(ctypes.byref(c), 0, None, None, None, None, None, None, 0, None) == MOE_OK
     assert L.moe_forward(ctypes.byref(c), 0, *([None] * 16), 0, None) == MOE_OK
     assert L.moe_combine(ctypes.byref(c), 0, None, None, None, None, None, None) == MOE_OK
+
+
+@pytest.mark.parametrize("name,tokens,stages", [
+    ("decode-bf16-T32", 32, ["route", "permute", "routed_up", "routed_down", "combine"]),
+    # a bf16 shared expert rides in the routed launches as one more group
+    ("skew-bf16-T16384", 16384, ["route", "permute", "routed_up", "routed_down", "combine"]),
+    # a shared expert of another type than the experts has launches of its own
+    ("fp8-T8192", 8192, ["route", "permute", "quant_x", "routed_up", "quant_h", "routed_down",
+                         "shared_up", "shared_down", "combine"]),
+    ("fp8-T8192", 64, ["route", "permute", "quant_x", "routed_up", "quant_h", "routed_down",
+                       "shared_up", "shared_down", "combine"]),
+    ("decode-fp4-T32", 32, ["route", "permute", "routed_up", "routed_down", "combine"]),
+    ("tiny-f32-T64", 64, ["route", "permute", "routed_up", "routed_down", "combine"]),
+])
+def test_forward_stage_mask(name, tokens, stages):
+    """moe_forward_stage_mask answers on the host which launches a forward runs."""
+    wl = WORKLOADS[name]
+    assert binding.stages_of(wl, tokens=tokens) == stages
+    assert binding.stages_of(wl, block=True, tokens=tokens) == ["norm"] + stages
+    m = ctypes.c_uint32(7)
+    c = binding.config_from(wl)
+    assert binding.lib().moe_forward_stage_mask(ctypes.byref(c), 0, ctypes.byref(m)) == MOE_OK
+    assert m.value == 0
 
 
 def test_static_forward_refuses_sizes_beyond_its_scratch():

@@ -19,8 +19,14 @@ RAGGED_FP4 = Workload("block-ragged-fp4-T77", 77, 256, 32, 4, 2, 4, 192, 320, "b
                       seed=42, shared_dtype="fp4")
 RAGGED_FP8 = Workload("block-ragged-fp8-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "fp8",
                       seed=43)
+# Hundreds of rows per expert: the 256 x 256 tile kernels, with the residual
+# added in the combine.
+BIG = Workload("block-big-groups-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "bf16",
+               seed=44)
+BIG_FP8 = Workload("block-big-groups-fp8-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp8",
+                   seed=45)
 CASES = [WORKLOADS["tiny-f32-T64"], RAGGED, RAGGED_FP4, RAGGED_FP8, WORKLOADS["decode-bf16-T32"],
-         WORKLOADS["decode-fp4-T32"]]
+         WORKLOADS["decode-fp4-T32"], BIG, BIG_FP8]
 
 
 @pytest.fixture(scope="module", autouse=True)
