@@ -69,7 +69,7 @@ __global__ __launch_bounds__(NORM_WAVES * WAVE) void rmsnorm_kernel(NormArgs p) 
       for (int q = 0; q < 4; ++q) {
         const float lo = (f[2 * q] * r) * g[2 * q];
         const float hi = (f[2 * q + 1] * r) * g[2 * q + 1];
-        o[q] = int(uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16));
+        o[q] = int(pack_bf16x2(lo, hi));
       }
     } else {
 #pragma unroll

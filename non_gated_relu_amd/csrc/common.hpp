@@ -21,11 +21,19 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// IEEE binary32 -> bfloat16, round to nearest, ties to even (finite inputs).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two IEEE binary32 values -> two bfloat16 (a in the low half), each rounded
+// to nearest, ties to even: one v_cvt_pk_bf16_f32 (gfx950's conversion rounds
+// as the mode register says, nearest even by default).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+// IEEE binary32 -> bfloat16, round to nearest, ties to even.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.0f));
 }
 
 // ---------------------------------------------------------------- waves

@@ -721,8 +721,8 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       }
       if (p.out_bf16) {
         uint2 w;
-        w.x = f32_to_bf16(v[0]) | (uint32_t(f32_to_bf16(v[1])) << 16);
-        w.y = f32_to_bf16(v[2]) | (uint32_t(f32_to_bf16(v[3])) << 16);
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + r * p.n + col) = w;
       } else {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + r * p.n + col) =

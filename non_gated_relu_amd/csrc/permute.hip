@@ -468,8 +468,8 @@ __global__ __launch_bounds__(PM_THREADS) void combine_kernel(CombineArgs p) {
     }
   }
   if (BF16_OUT) {
-    uint32_t lo = f32_to_bf16(acc[0]) | (uint32_t(f32_to_bf16(acc[1])) << 16);
-    uint32_t hi = f32_to_bf16(acc[2]) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    uint32_t lo = pack_bf16x2(acc[0], acc[1]);
+    uint32_t hi = pack_bf16x2(acc[2], acc[3]);
     reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.hidden)[c] = make_uint2(lo, hi);
   } else {
     reinterpret_cast<f32x4_t*>(static_cast<float*>(p.y) + t * p.hidden)[c] = acc;

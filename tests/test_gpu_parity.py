@@ -429,3 +429,43 @@ def test_concurrent_calls_on_two_streams(wl):
             yb = lb(xb)
         torch.cuda.synchronize()
         assert torch.equal(_bits(ya), _bits(ref_a)) and torch.equal(_bits(yb), _bits(ref_b))
+
+
+def test_bf16_rounding_is_nearest_even():
+    """The kernels' fp32 -> bf16 rounding (one hardware conversion, shared by
+    every epilogue) against the oracle's nearest-even rounding, bit for bit.
+    moe_combine with one slot of weight 1 and no shared rows returns
+    round(fma(1, v, 0)) = round(v) for any fp32 v: exact ties with an even and
+    an odd upper half, one ulp either side of them, subnormals, the largest
+    finite values (a tie above the largest bf16 rounds to infinity), signed
+    zeros and random finite patterns."""
+    rng = np.random.default_rng(5)
+    d = 256
+    n = 64 * d
+
+    def finite(u):
+        return u[((u >> 23) & 0xFF) != 0xFF]
+
+    hi = rng.integers(0, 1 << 16, size=n, dtype=np.uint64).astype(np.uint32) << 16
+    pats = [finite(rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)),
+            finite(hi | 0x8000), finite(hi | 0x7FFF), finite(hi | 0x8001),
+            (rng.integers(0, 1 << 23, size=4096, dtype=np.uint64).astype(np.uint32) |
+             (rng.integers(0, 2, size=4096, dtype=np.uint64).astype(np.uint32) << 31)),
+            np.array([0x00008000, 0x00018000, 0x007F8000, 0x80008000, 0x7F7F7FFF, 0x7F7F8000,
+                      0x7F7FFFFF, 0x7F7E8000, 0xFF7F8000, 0xFF7E8000, 0x00000000, 0x80000000,
+                      0x00000001, 0x3F808000, 0x3F818000], dtype=np.uint32)]
+    u = np.concatenate(pats)
+    u = np.concatenate([u, np.zeros((-u.size) % d, np.uint32)])
+    v = u.view(np.float32)
+    T = v.size // d
+    wl = Workload("bf16-rounding", T, d, 16, 1, 1, 1, 64, 0, "bf16", "bf16")
+    cfg = binding.config_from(wl)
+    y_perm = torch.from_numpy(v.reshape(T, d).copy()).cuda()
+    w = torch.ones((T, 1), dtype=torch.float32, device="cuda")
+    slot_pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    y = binding.combine(cfg, slot_pos, w, y_perm)
+    torch.cuda.synchronize()
+    got = y.view(torch.int16).cpu().numpy().astype(np.uint16).reshape(-1)
+    ref = oracle.bf16_round(v.astype(np.float64) * 1.0 + 0.0).reshape(-1)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, [(hex(int(u[i])), hex(int(got[i])), hex(int(ref[i]))) for i in bad[:8]]
