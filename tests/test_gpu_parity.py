@@ -167,13 +167,18 @@ def test_small_layer_every_entry_point(wl):
     # the layer against the oracle
     assert_close_rms(got, ref["y"], f"{wl.name} layer", **_tol(wl), row_allow=allow_tok)
 
-    # the fused entry point equals the composition bit for bit
+    # the fused entry point equals the composition bit for bit, routing included
+    # (decode-sized calls select and permute in one launch of their own)
     su, sd = _scales(t, wl)
     ssu, ssd = t.get("ws_up_bscale"), t.get("ws_down_bscale")
+    f_idx = torch.empty_like(parts["idx"])
+    f_w = torch.empty_like(parts["w"])
     y = binding.forward(cfg, t["x"], t["w_gate"], t["e_bias"], t["w_up"], t["w_down"],
                         t.get("ws_up"), t.get("ws_down"), su, sd, ws_up_scale=ssu,
-                        ws_down_scale=ssd)
+                        ws_down_scale=ssd, topk_idx=f_idx, topk_w=f_w)
     torch.cuda.synchronize()
+    assert torch.equal(f_idx, parts["idx"])
+    assert torch.equal(f_w.view(torch.int32), parts["w"].view(torch.int32))
     assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
                        parts["y"].view(torch.int16) if y.dtype == torch.bfloat16 else parts["y"])
 
@@ -226,6 +231,25 @@ def test_exact_ties_go_to_the_lowest_index():
     torch.cuda.synchronize()
     assert (idx.cpu().numpy() == np.arange(wl.top_k)).all()
     np.testing.assert_allclose(w.cpu().numpy(), 2.5 / wl.top_k, rtol=1e-7)
+
+
+@pytest.mark.parametrize("wl", [WORKLOADS["decode-bf16-T32"].with_tokens(20), ALL_GROUPS,
+                                WORKLOADS["tiny-f32-T64"]], ids=lambda w: f"{w.name}-T{w.tokens}")
+def test_exact_ties_in_the_forward_selection(wl):
+    """All logits and biases zero: every score ties, so the lowest groups and
+    then the lowest expert ids win, each with weight scale / k; through
+    moe_forward, whose decode-sized calls select inside the permute launch."""
+    inp = make_inputs(wl)
+    inp["w_gate"] = np.zeros_like(inp["w_gate"])
+    inp["e_bias"] = np.zeros_like(inp["e_bias"])
+    layer = binding.MoELayer(wl, inp)
+    x = binding.to_device(inp["x"], "cuda", "x", wl)
+    layer(x)
+    torch.cuda.synchronize()
+    ref_idx, ref_w, margin = oracle.route(wl, inp["x"], inp["w_gate"], inp["e_bias"])
+    assert (ref_idx == np.arange(wl.top_k)).all()
+    assert np.array_equal(layer.topk_idx[:wl.tokens].cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(layer.topk_w[:wl.tokens].cpu().numpy(), 2.5 / wl.top_k, rtol=1e-7)
 
 
 def test_zero_tokens_and_growing_calls_reuse_one_workspace():
