@@ -26,7 +26,7 @@
 //    64-byte slices fetched straight into a 4-stage LDS ring; fp8 keeps the
 //    weight rows two 128-byte steps ahead, the activation rows one);
 //  * the router's logits (a dense GEMM against the small gate matrix):
-//    gemm_stream_kernel, thin tiles over a DMA ring;
+//    gemm_stream_kernel, 16- to 64-row tiles over a DMA ring;
 //  * MXFP4 weights: gemm_fp4_kernel (16- or 64-row tiles).
 // Every output element accumulates its K steps in ascending order with the
 // same MFMA, whichever tile shape computes it (for fp4: the same order for
@@ -740,28 +740,31 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
 
 // ---------------------------------------------------------- stream kernel
 //
-// Thin (16-row) tiles of bf16 GEMMs that stream their weights: the expert
-// MLPs at decode, where an expert sees a handful of rows, and the router's
-// logits.  There is little MFMA work per byte, so what matters is how many
-// bytes each CU keeps in flight: K moves in 64-byte row slices (the ring
-// kernel's swizzled 1 KB block layout) through a ring of SK_RING LDS stages
-// filled by global_load_lds_dwordx4 SK_RING - 1 stages ahead, with no
-// staging registers; at 9 KB a stage that is about 125 KB in flight per CU.
-// Same MFMA and per-lane K bytes as gemm_kernel, so the same results.
-constexpr int SK_BM = 16;
+// Thin tiles (16, 32 or 64 rows) of bf16 GEMMs that stream their operands:
+// the router's logits, where the gate matrix is small and every tile reads
+// all of it.  There is little MFMA work per byte, so what matters is how many bytes
+// each CU keeps in flight: K moves in 64-byte row slices (the ring kernel's
+// swizzled 1 KB block layout) through a ring of SK_RING LDS stages filled by
+// global_load_lds_dwordx4 SK_RING - 1 stages ahead, with no staging
+// registers.  A stage is FM activation blocks and BN / 16 weight blocks (9 KB
+// for 16 x 128 tiles, 12 KB for 64 x 128).  Wider tiles re-read the weights
+// from L2 less often.  Same MFMA and per-lane K bytes as gemm_kernel, so the
+// same results whatever the tile.
 constexpr int SK_RING = 8;
 
-template <int KIND, int BN, int EPI>
+template <int KIND, int FM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
   static_assert(KIND == K_BF16, "the stream kernel takes bf16 operands");
-  constexpr int NBLK = 1 + BN / 16;          // 1 KB blocks per stage: A, then B
+  constexpr int BM = 16 * FM;
+  constexpr int NBLK = FM + BN / 16;         // 1 KB blocks per stage: A, then B
   constexpr int STAGE = NBLK * 1024;
   constexpr int FN = BN / 64;                // column fragments per wave (4 waves along N)
   constexpr int MAXQ = (NBLK + 3) / 4;       // blocks one wave fetches per stage, at most
+  static_assert(MAXQ <= 3, "the waits below count at most three fetches per stage");
   __shared__ __attribute__((aligned(1024))) char ring[SK_RING * STAGE];
 
   Tile t;
-  if (!locate_tile<SK_BM, BN>(pa, t, blockIdx.x)) return;
+  if (!locate_tile<BM, BN>(pa, t, blockIdx.x)) return;
   const GemmProblem& p = t.p;
   const int wave = threadIdx.x / WAVE;
   const int lane = lane_id();
@@ -777,11 +780,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
 #pragma unroll
   for (int q = 0; q < MAXQ; ++q) {
     const int blk = min(wave + 4 * q, NBLK - 1);
-    if (blk == 0) {
-      const int64_t r = min<int64_t>(t.m0 + r_in, t.gend - 1);
+    if (blk < FM) {
+      const int64_t r = min<int64_t>(t.m0 + blk * 16 + r_in, t.gend - 1);
       src[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
     } else {
-      const int n = min(t.n0 + (blk - 1) * 16 + r_in, p.n - 1);
+      const int n = min(t.n0 + (blk - FM) * 16 + r_in, p.n - 1);
       src[q] = wbase + int64_t(n) * kbytes + chunk * 16;
     }
   }
@@ -811,9 +814,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
   const int lofs = lrow * RG_ROWB + ((lgrp ^ rg_swizzle(lrow)) * 16);
-  f32x4_t acc[FN];
+  f32x4_t acc[FM][FN];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
   for (int s = 0; s < SK_RING - 1; ++s) dma(s, ring + s * STAGE);
@@ -822,20 +827,26 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs pa) {
     block_sync_lds();  // stage s is in LDS for all waves; slot (s - 1) % SK_RING is free
     dma(s + SK_RING - 1, ring + ((s + SK_RING - 1) % SK_RING) * STAGE);
     const char* buf = ring + (s % SK_RING) * STAGE;
-    const i32x4_t af = *reinterpret_cast<const i32x4_t*>(buf + lofs);
-    i32x4_t bf[FN];
+    i32x4_t af[FM], bf[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const i32x4_t*>(buf + i * 1024 + lofs);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      bf[j] = *reinterpret_cast<const i32x4_t*>(buf + (1 + wave * FN + j) * 1024 + lofs);
+      bf[j] = *reinterpret_cast<const i32x4_t*>(buf + (FM + wave * FN + j) * 1024 + lofs);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[j] = mfma_bf16(af, bf[j], acc[j]);
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_bf16(af[i], bf[j], acc[i][j]);
   }
   // no LDS write may still be in flight when the workgroup ends
   __builtin_amdgcn_s_waitcnt(WAIT_VM0);
 
 #pragma unroll
-  for (int j = 0; j < FN; ++j)
-    store_block<KIND, EPI>(t, acc[j], t.m0 + lgrp * 4, t.n0 + (wave * FN + j) * 16 + lrow);
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      store_block<KIND, EPI>(t, acc[i][j], t.m0 + 16 * i + lgrp * 4,
+                             t.n0 + (wave * FN + j) * 16 + lrow);
 }
 
 // ------------------------------------------------------------ fp4 kernel
@@ -1263,8 +1274,14 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
                            Timing t) {
   const dim3 g(grid);
   if constexpr (KIND == K_BF16) {
-    if (shape.stream && shape.bm == SK_BM && shape.bn == 128)
-      return launch_k(gemm_stream_kernel<KIND, 128, EPI>, g, dim3(256), stream, t, p);
+    if (shape.stream && shape.bn == 128) {
+      if (shape.bm == 16)
+        return launch_k(gemm_stream_kernel<KIND, 1, 128, EPI>, g, dim3(256), stream, t, p);
+      if (shape.bm == 32)
+        return launch_k(gemm_stream_kernel<KIND, 2, 128, EPI>, g, dim3(256), stream, t, p);
+      if (shape.bm == 64)
+        return launch_k(gemm_stream_kernel<KIND, 4, 128, EPI>, g, dim3(256), stream, t, p);
+    }
   }
   if constexpr (KIND == K_BF16) {
     // decode tiles; its buffer offsets are 32-bit, else gemm_kernel below

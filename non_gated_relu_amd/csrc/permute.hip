@@ -91,32 +91,40 @@ __device__ void place_chunk(const int32_t* ids, int64_t s_begin, int n, int E, i
 }
 
 // Exclusive scan of n <= PM_THREADS * 4 values held in LDS `v` (in place);
-// returns the total.  All threads must call.
+// returns the total.  All threads must call.  Each thread owns 4 consecutive
+// entries; a wave scans its threads' sums with shuffles, and the waves'
+// totals are added through LDS (two barriers in all).
 __device__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* tmp) {
-  // each thread owns 4 consecutive entries
   const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = t / WAVE;
   int32_t loc[4];
   int32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int j = t * 4 + i;
+    const int j = t * 4 + i;
     loc[i] = j < n ? v[j] : 0;
     sum += loc[i];
   }
-  tmp[t] = sum;
-  __syncthreads();
-  // Hillis-Steele over PM_THREADS partial sums
-  for (int off = 1; off < PM_THREADS; off <<= 1) {
-    int32_t add = t >= off ? tmp[t - off] : 0;
-    __syncthreads();
-    tmp[t] += add;
-    __syncthreads();
+  int32_t incl = sum;  // inclusive scan of the sums over the wave's lanes
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const int32_t up = __shfl_up(incl, off);
+    if (lane >= off) incl += up;
   }
-  int32_t run = tmp[t] - sum;
-  const int32_t total = tmp[PM_THREADS - 1];
+  if (lane == WAVE - 1) tmp[wave] = incl;
+  __syncthreads();
+  int32_t run = incl - sum;
+  int32_t total = 0;
+#pragma unroll
+  for (int w = 0; w < PM_WAVES; ++w) {
+    const int32_t wt = tmp[w];
+    if (w < wave) run += wt;
+    total += wt;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int j = t * 4 + i;
+    const int j = t * 4 + i;
     if (j < n) v[j] = run;
     run += loc[i];
   }
@@ -127,6 +135,10 @@ __device__ int32_t block_exclusive_scan(int32_t* v, int n, int32_t* tmp) {
 // M-tile schedule of a grouped GEMM (layout in internal.hpp): group g covers
 // the rows range(g) = [a, b); tiles of `bm` rows, groups in order, then the
 // optional extra group.  All threads must call; tiles/tmp are LDS scratch.
+// After the scan of the groups' tile counts, each thread writes whole tiles:
+// tile j belongs to the last group whose first tile is at or before j
+// (groups without tiles share their successor's first tile), found by a
+// binary search, so a group with many tiles costs no thread more than others.
 template <typename Range>
 __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp, int32_t* tiles,
                               int32_t* tmp, int32_t* carry) {
@@ -141,15 +153,22 @@ __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp,
     }
     __syncthreads();
     const int32_t total = block_exclusive_scan(tiles, n, tmp);
-    for (int i = threadIdx.x; i < n; i += PM_THREADS) {
+    const int32_t base = *carry;
+    for (int32_t j = threadIdx.x; j < total; j += PM_THREADS) {
+      int lo = 0, hi = n - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tiles[mid] <= j)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
       int64_t a, b;
-      range(g0 + i, a, b);
-      int32_t at = *carry + tiles[i];
-      for (int64_t m = a; m < b; m += sp.bm, ++at) {
-        if (at < sp.max_tiles) {
-          sp.sched[2 + 2 * at] = g0 + i;
-          sp.sched[3 + 2 * at] = static_cast<int32_t>(m);
-        }
+      range(g0 + lo, a, b);
+      const int32_t at = base + j;
+      if (at < sp.max_tiles) {
+        sp.sched[2 + 2 * at] = g0 + lo;
+        sp.sched[3 + 2 * at] = static_cast<int32_t>(a + int64_t(j - tiles[lo]) * sp.bm);
       }
     }
     __syncthreads();
@@ -262,100 +281,90 @@ __global__ __launch_bounds__(PM_THREADS) void permute_hist_kernel(PermuteArgs p)
 }
 
 // Pass 2 (one workgroup): per-expert totals, offsets, each chunk's base, and
-// the GEMM schedule.  The chunk counts are scanned in LDS when they fit
-// (n_chunks * E <= PM_SCAN_LDS), with coalesced loads and stores: H =
-// PM_THREADS / E threads share an expert's column, each scanning a run of
-// consecutive chunks, and the runs' totals are then added in order.
-// Otherwise each expert's column is walked in global memory.
-constexpr int PM_SCAN_LDS = 16384;
+// the GEMM schedule.  H = PM_THREADS / E threads share an expert's column of
+// chunk counts, each owning a run of consecutive chunks.  When a run fits in
+// registers (at most PM_SCAN_REG chunks) a thread issues the loads of its
+// whole run before using any (coalesced: the threads of one run index are
+// consecutive experts),
+// scans it in registers, and writes each chunk's final base once the runs'
+// totals and the expert offsets are known.  Otherwise each expert's column
+// is walked in global memory.
+constexpr int PM_SCAN_REG = 48;  // loads in flight per thread (vmcnt counts to 63)
 __global__ __launch_bounds__(PM_THREADS) void permute_scan_kernel(PermuteArgs p) {
   __shared__ int32_t off[1024];
   __shared__ int32_t cnt[1024];
   __shared__ int32_t tiles[1024];
   __shared__ int32_t tmp[PM_THREADS];
   __shared__ int32_t run_total[PM_THREADS];
-  __shared__ int32_t run_base[PM_THREADS];
-  __shared__ int32_t bc[PM_SCAN_LDS];
   __shared__ int32_t carry;
   const int E = p.n_experts;
-  const int nb = p.n_chunks * E;
-  const bool in_lds = nb <= PM_SCAN_LDS;
   const int H = E <= PM_THREADS ? PM_THREADS / E : 1;  // threads per expert column
   const int per = (p.n_chunks + H - 1) / H;            // chunks per run
-  if (in_lds) {
-    constexpr int B = 8;  // loads in flight per thread
-    for (int i0 = 0; i0 < nb; i0 += B * PM_THREADS) {
-      int32_t v[B];
+  const bool in_reg = E <= PM_THREADS && per <= PM_SCAN_REG;
+  const int e = threadIdx.x % E;
+  const int h = threadIdx.x / E;  // run h of expert e's column (none when h >= H)
+  const int b0 = h * per;
+  const int nrun = h < H ? max(min(per, p.n_chunks - b0), 0) : 0;  // chunks in this run
+  int32_t v[PM_SCAN_REG];
+  int32_t before = 0;  // the counts of expert e in chunks before this run
+  if (in_reg) {
+    // every load is issued (from a clamped, valid chunk) before the first use
+    const int last = p.n_chunks - 1;
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int i = i0 + u * PM_THREADS + threadIdx.x;
-        v[u] = i < nb ? p.block_counts[i] : 0;
-      }
+    for (int u = 0; u < PM_SCAN_REG; ++u) v[u] = p.block_counts[min(b0 + u, last) * E + e];
 #pragma unroll
-      for (int u = 0; u < B; ++u) {
-        const int i = i0 + u * PM_THREADS + threadIdx.x;
-        if (i < nb) bc[i] = v[u];
-      }
+    for (int u = 0; u < PM_SCAN_REG; ++u) v[u] = u < nrun ? v[u] : 0;
+    int32_t total = 0;
+#pragma unroll
+    for (int u = 0; u < PM_SCAN_REG; ++u) {
+      const int32_t c = v[u];
+      v[u] = total;  // the chunk's base inside its run
+      total += c;
     }
-    __syncthreads();
-    const int e = threadIdx.x % E;
-    const int h = threadIdx.x / E;  // run h of expert e's column (none when h >= H)
-    if (h < H) {
-      int32_t total = 0;
-      const int b_end = min((h + 1) * per, p.n_chunks);
-      for (int b = h * per; b < b_end; ++b) {
-        const int32_t v = bc[b * E + e];
-        bc[b * E + e] = total;  // the chunk's base inside its run
-        total += v;
-      }
-      run_total[h * E + e] = total;
-    }
+    if (h < H) run_total[h * E + e] = total;
     __syncthreads();
     if (h < H) {
-      int32_t before = 0;
       for (int j = 0; j < h; ++j) before += run_total[j * E + e];
-      run_base[h * E + e] = before;
       if (h == H - 1) {
-        const int32_t total = before + run_total[h * E + e];
-        p.expert_counts[e] = total;
-        off[e] = total;
-        cnt[e] = total;
+        const int32_t all = before + total;
+        p.expert_counts[e] = all;
+        off[e] = all;
+        cnt[e] = all;
       }
     }
   } else {
     constexpr int B = 8;  // chunk counts loaded per batch
-    for (int e = threadIdx.x; e < E; e += PM_THREADS) {
+    for (int x = threadIdx.x; x < E; x += PM_THREADS) {
       int32_t total = 0;
-      for (int b0 = 0; b0 < p.n_chunks; b0 += B) {
-        int32_t v[B];
+      for (int c0 = 0; c0 < p.n_chunks; c0 += B) {
+        int32_t w[B];
 #pragma unroll
         for (int u = 0; u < B; ++u)
-          v[u] = b0 + u < p.n_chunks ? p.block_counts[(b0 + u) * E + e] : 0;
+          w[u] = c0 + u < p.n_chunks ? p.block_counts[(c0 + u) * E + x] : 0;
 #pragma unroll
         for (int u = 0; u < B; ++u) {
-          if (b0 + u < p.n_chunks) {
-            p.block_counts[(b0 + u) * E + e] = total;
-            total += v[u];
+          if (c0 + u < p.n_chunks) {
+            p.block_counts[(c0 + u) * E + x] = total;
+            total += w[u];
           }
         }
       }
-      p.expert_counts[e] = total;
-      off[e] = total;
-      cnt[e] = total;
+      p.expert_counts[x] = total;
+      off[x] = total;
+      cnt[x] = total;
     }
   }
   __syncthreads();
   block_exclusive_scan(off, E, tmp);
-  for (int e = threadIdx.x; e < E; e += PM_THREADS) p.expert_offsets[e] = off[e];
-  if (in_lds) {
-    for (int i = threadIdx.x; i < nb; i += PM_THREADS) {
-      const int b = i / E;
-      const int e = i - b * E;
-      p.block_counts[i] = bc[i] + run_base[(b / per) * E + e] + off[e];
-    }
+  for (int x = threadIdx.x; x < E; x += PM_THREADS) p.expert_offsets[x] = off[x];
+  if (in_reg) {
+    const int32_t base = before + off[e];
+#pragma unroll
+    for (int u = 0; u < PM_SCAN_REG; ++u)
+      if (u < nrun) p.block_counts[(b0 + u) * E + e] = v[u] + base;
   } else {
-    for (int e = threadIdx.x; e < E; e += PM_THREADS)
-      for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + e] += off[e];
+    for (int x = threadIdx.x; x < E; x += PM_THREADS)
+      for (int b = 0; b < p.n_chunks; ++b) p.block_counts[b * E + x] += off[x];
   }
   if (threadIdx.x == 0) p.expert_offsets[E] = static_cast<int32_t>(p.slots);
   if (p.sched.sched)

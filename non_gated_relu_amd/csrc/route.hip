@@ -166,11 +166,12 @@ hipError_t launch_route(const RouteArgs& p, int kind, int mode, hipStream_t stre
     q.index_div = 1;
     g.sched = nullptr;
     g.n_groups = 1;
-    // Every M tile streams the whole (small, E x d) gate matrix from L2: thin
-    // tiles through the DMA-ring kernel keep the most of it in flight up to
-    // some 8k tokens; beyond, 64-row tiles re-read it less often.  Every
-    // shape gives the same logits (one MFMA chain per element, K ascending).
-    const GemmShape shape = p.tokens <= 8192 ? GemmShape{16, 128, true} : GemmShape{64, 128};
+    // Every M tile streams the whole (small, E x d) gate matrix from L2
+    // through the DMA-ring kernel: the widest tile (16, 32 or 64 rows) that
+    // still gives every CU a tile re-reads it least.  Every shape gives the
+    // same logits (one MFMA chain per element, K ascending).
+    const int bm = p.tokens >= 256 * 64 ? 64 : p.tokens >= 256 * 32 ? 32 : 16;
+    const GemmShape shape{bm, 128, true};
     g.n_tiles = (p.n_experts + shape.bn - 1) / shape.bn;
     const int64_t mtiles = (p.tokens + shape.bm - 1) / shape.bm;
     e = launch_gemm(g, kind, EPI_PLAIN, shape, mtiles, 0, stream, first);
