@@ -170,22 +170,22 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& pa, Tile& t, int bid
       nt = b - mt * pa.n_tiles;
       if (mt >= first) return false;
     }
-    gs = pa.sched[2 + 2 * mt];
+    const int32_t e = pa.sched[2 + 2 * mt];
+    gs = e & 0xFFFF;
     t.m0 = pa.sched[3 + 2 * mt];
+    t.gend = t.m0 + (e >> 16);  // the tile's rows, from the schedule
   } else {  // dense: one group, tiles in row order
     gs = 0;
     t.m0 = int64_t(mt) * BM;
     if (t.m0 >= pa.prob[0].rows) return false;
+    t.gend = pa.prob[0].rows;
   }
   // schedule group n_groups is the single group of the second problem
   const bool second = gs >= pa.n_groups;
   t.p = pick_problem(pa, second);
   t.g = second ? 0 : gs;
-  const GemmProblem& p = t.p;
-  // no offsets: a single group spans every row
-  t.gend = p.offsets ? min<int64_t>(max<int64_t>(p.offsets[t.g + 1], 0), p.rows) : p.rows;
   t.n0 = nt * BN;
-  return t.n0 < p.n;
+  return t.n0 < t.p.n;
 }
 
 __device__ __forceinline__ int64_t src_row(const GemmProblem& p, int64_t r) {
@@ -372,6 +372,7 @@ __device__ __forceinline__ int rg_swizzle(int r) { return 3 * ((r >> 3) & 1); }
 
 #define MOE_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+
 // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
 constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
@@ -424,14 +425,35 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   const int r_in = lane >> 2;
   const int chunk = (lane & 3) ^ rg_swizzle(r_in);
   const char* wbase = static_cast<const char*>(p.w) + int64_t(t.g) * p.n * kbytes;
+  // (blocks w + NW q with q < 16 / NW are A rows, the rest B rows; the A
+  // rows' permutation indices are all loaded before any is used, from a
+  // harmless address when the problem has no permutation)
+  static_assert(16 % NW == 0, "A and B blocks split by q");
+  constexpr int QA = 16 / NW;
+  // (fp8, whose registers are full, resolves them one at a time)
   const char* src[DMA_PER_WAVE];
+  int32_t perm[QA];
+  if constexpr (KIND != K_FP8) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q) {
+      const int64_t r = min<int64_t>(t.m0 + (wave + NW * q) * 16 + r_in, t.gend - 1);
+      perm[q] = *(p.row_index ? p.row_index + r : static_cast<const int32_t*>(p.a));
+    }
+  }
 #pragma unroll
   for (int q = 0; q < DMA_PER_WAVE; ++q) {
     const int blk = wave + NW * q;
     const int row = (blk % 16) * 16 + r_in;
-    if (blk < 16) {
-      const int64_t r = min<int64_t>(t.m0 + row, t.gend - 1);
-      src[q] = static_cast<const char*>(p.a) + src_row(p, r) * kbytes + chunk * 16;
+    if (KIND == K_FP8 ? blk < 16 : q < QA) {
+      int64_t a_row;
+      if constexpr (KIND == K_FP8) {
+        a_row = src_row(p, min<int64_t>(t.m0 + row, t.gend - 1));
+      } else {
+        const int64_t r = min<int64_t>(t.m0 + row, t.gend - 1);
+        a_row = p.row_index ? int64_t(perm[q] / p.index_div) : r;
+        a_row = min<int64_t>(max<int64_t>(a_row, 0), p.a_rows - 1);
+      }
+      src[q] = static_cast<const char*>(p.a) + a_row * kbytes + chunk * 16;
     } else {
       const int n = min(t.n0 + row, p.n - 1);
       src[q] = wbase + int64_t(n) * kbytes + chunk * 16;
@@ -558,10 +580,10 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // (the first RING - 1 stages are fetched before the loop instance is
+  // chosen, which waits for the group's extent)
   auto k_loop = [&](auto fmv_c, auto full_c) {
     i32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
-#pragma unroll
-    for (int s = 0; s < RING - 1; ++s) dma(s, ring + s * RG_STAGE);
     __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
     block_sync_lds();
 #pragma unroll
@@ -697,24 +719,33 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     sc_row[threadIdx.x] = my_scale;
     __syncthreads();
   } else {
+#pragma unroll
+    for (int s = 0; s < RING - 1; ++s) dma(s, ring + s * RG_STAGE);
     run(k_loop);
   }
 
   // Epilogue: the same arithmetic as store_block, fp8 scales from LDS.  The
   // MFMAs take the weight fragment as their first operand, so a lane holds
   // the transposed block: one row and four consecutive columns, written
-  // with one 8-byte (bf16) or 16-byte (fp32) store.
+  // with one 8-byte (bf16) or 16-byte (fp32) store.  Each row fragment
+  // computes one address; a wave's column blocks are 16 WN columns apart,
+  // constant offsets from it.  N is a multiple of 16, so whether a column
+  // block lies inside N is the same for every lane of the wave.
+  const int nvalid = min(p.n - t.n0, RG_BN);
+  const int c0 = wn * 16 + lgrp * 4;  // tile-local first column of block j = 0
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int rl = (wm + WM * i) * 16 + lrow;  // tile-local row
     const int64_t r = t.m0 + rl;
     if (r >= t.gend) continue;
     const float sa = KIND == K_FP8 ? sc_row[rl] : 1.0f;
+    const int64_t e0 = r * p.n + t.n0 + c0;  // output element of block j = 0
+    uint16_t* const row16 = static_cast<uint16_t*>(p.out) + e0;
+    float* const row32 = static_cast<float*>(p.out) + e0;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int cl = (wn + WN * j) * 16 + lgrp * 4;  // tile-local first column
-      const int col = t.n0 + cl;
-      if (col >= p.n) continue;  // N is a multiple of 16: a block is all in or all out
+      if ((wn + WN * j) * 16 >= nvalid) continue;
+      const int cl = c0 + WN * 16 * j;
       float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -729,10 +760,9 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
         uint2 w;
         w.x = pack_bf16x2(v[0], v[1]);
         w.y = pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + r * p.n + col) = w;
+        *reinterpret_cast<uint2*>(row16 + WN * 16 * j) = w;
       } else {
-        *reinterpret_cast<f32x4_t*>(static_cast<float*>(p.out) + r * p.n + col) =
-            f32x4_t{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4_t*>(row32 + WN * 16 * j) = f32x4_t{v[0], v[1], v[2], v[3]};
       }
     }
   }

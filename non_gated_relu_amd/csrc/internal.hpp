@@ -49,9 +49,12 @@ struct RouteArgs {
 
 // M-tile schedule of a grouped GEMM: sched[0] = tile count, sched[1] = the
 // tiles of the first problem's groups (they come first); entry i at
-// sched[2+2i] = group, sched[3+2i] = first problem row.  Tiles of a group are
-// consecutive and groups come in order; the optional extra group (index
-// n_groups) covers rows [0, extra_rows) of the second problem.
+// sched[2+2i] = group | (rows of the tile << 16), sched[3+2i] = first problem
+// row.  A tile's rows are min(bm, rows left in its group), so a GEMM knows
+// where its tile's group ends without reading the group offsets.  Tiles of a
+// group are consecutive and groups come in order; the optional extra group
+// (index n_groups) covers rows [0, extra_rows) of the second problem.
+// Groups are fewer than 2^16 and bm at most 2^15.
 struct ScheduleSpec {
   int32_t* sched;      // [2 + 2*max_tiles], or null (no schedule wanted)
   int64_t extra_rows;  // rows of the extra group (0 = none)

@@ -167,8 +167,10 @@ __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp,
       range(g0 + lo, a, b);
       const int32_t at = base + j;
       if (at < sp.max_tiles) {
-        sp.sched[2 + 2 * at] = g0 + lo;
-        sp.sched[3 + 2 * at] = static_cast<int32_t>(a + int64_t(j - tiles[lo]) * sp.bm);
+        const int64_t m = a + int64_t(j - tiles[lo]) * sp.bm;
+        const int32_t rows = static_cast<int32_t>(min<int64_t>(sp.bm, b - m));
+        sp.sched[2 + 2 * at] = (g0 + lo) | (rows << 16);
+        sp.sched[3 + 2 * at] = static_cast<int32_t>(m);
       }
     }
     __syncthreads();
@@ -180,7 +182,8 @@ __device__ void emit_schedule(Range range, int n_groups, const ScheduleSpec& sp,
   for (int j = threadIdx.x; j < extra; j += PM_THREADS) {
     const int32_t at = *carry + j;
     if (at < sp.max_tiles) {
-      sp.sched[2 + 2 * at] = n_groups;
+      const int32_t rows = static_cast<int32_t>(min<int64_t>(sp.bm, sp.extra_rows - int64_t(j) * sp.bm));
+      sp.sched[2 + 2 * at] = n_groups | (rows << 16);
       sp.sched[3 + 2 * at] = j * sp.bm;
     }
   }
