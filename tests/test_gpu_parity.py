@@ -370,6 +370,63 @@ def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
     assert_close_rms(to_f64(big), ref, f"{wl.name} expert_ffn 256-row tiles", row_allow=allow)
 
 
+# 256-row tiles at the edges of the ring kernels: groups whose last tile holds
+# 1 to 17 rows (so one row of waves has no rows of its own), empty groups, and
+# enough tiles (at least two per compute unit) for the persistent bf16 launch.
+EDGE_TILE_ROWS = [1, 10, 16, 17, 255, 0, 129, 3, 64, 200, 33, 1, 16, 90, 7, 250]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_ring_tiles_with_few_rows(dt):
+    """Rows in 256-row tiles that end 1..17 rows into a tile, over a launch
+    large enough for the persistent ring kernel: the oracle's rows within the
+    gates, and the bits of the same rows computed in 16-row tiles."""
+    # the Nemotron-H expert shape (hidden 2688, intermediate 1856) over 16 experts
+    wl = Workload(f"edge-tiles-{dt}", 4096, 2688, 16, 4, 1, 2, 1856, 0, "bf16", dt, seed=41)
+    print(f"case {wl.name}", flush=True)
+    inp = make_inputs(wl)
+    t = upload(inp, wl)
+    cfg = binding.config_from(wl)
+    sizes = np.array([256 * (g % 9) + r if r else 0 for g, r in enumerate(EDGE_TILE_ROWS)])
+    sizes[sizes.argmax()] += 256 * 60  # one hot expert: more tiles than compute units
+    offsets = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    S = int(offsets[-1])
+    rng = np.random.default_rng(41)
+    src = rng.integers(0, wl.tokens, size=S).astype(np.int32)
+    su, sd = _scales(t, wl)
+    sc = dict(w_dtype=dt, w_up_scale=su, w_down_scale=sd)
+    big = binding.expert_ffn(cfg, t["w_up"], t["w_down"], t["x"],
+                             torch.from_numpy(offsets).cuda(), S,
+                             row_index=torch.from_numpy(src).cuda(), **sc)
+    # rows sampled from every group: its first and last rows, the last tile's
+    # rows, and random rows
+    pick = []
+    for g in range(wl.n_experts):
+        a, b = int(offsets[g]), int(offsets[g + 1])
+        if b > a:
+            pick += [a, b - 1] + list(range(max(a, b - 17), b))
+            pick += list(rng.integers(a, b, size=8))
+    pick = np.unique(np.array(pick))
+    mats = np.searchsorted(offsets, pick, side="right") - 1
+    counts = np.bincount(mats, minlength=wl.n_experts).astype(np.int32)
+    small_off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    small = binding.expert_ffn(cfg, t["w_up"], t["w_down"], t["x"],
+                               torch.from_numpy(small_off).cuda(), int(pick.size),
+                               row_index=torch.from_numpy(src[pick]).cuda(), **sc)
+    torch.cuda.synchronize()
+    got = big[torch.from_numpy(pick).cuda().long()]
+    assert torch.equal(got, small), "256-row tiles and 16-row tiles differ"
+    fp8 = dt == "fp8"
+    bu, bd = _scales(inp, wl)
+    ref = oracle.ffn_rows(inp["x"], wl.act_dtype, src[pick], mats, inp["w_up"], inp["w_down"], dt,
+                          bu if fp8 else None, bd if fp8 else None, quant_a=fp8)
+    allow = None
+    if fp8:
+        allow = fp8_flips.row_allowance(inp["x"], src[pick], mats, inp["w_up"],
+                                        inp["w_up_scale"], inp["w_down"], inp["w_down_scale"])
+    assert_close_rms(to_f64(got), ref, f"{wl.name} expert_ffn, {pick.size} rows", row_allow=allow)
+
+
 @pytest.mark.parametrize("T,k,E,skew", [(1500, 6, 128, False), (4097, 6, 128, True),
                                         (16384, 6, 128, True), (3000, 3, 16, False),
                                         (2000, 4, 48, True), (5000, 8, 256, False)])
