@@ -30,9 +30,9 @@ namespace {
 
 constexpr int64_t ROUTE_WAVES_MAX_TOKENS = 64;     // up to here: one wave per logit block
 constexpr int64_t ROUTE_DIRECT_MAX_TOKENS = 2048;  // beyond: router logits as a GEMM
-// up to here moe_forward selects and permutes in one launch (each of its four
+// up to here moe_forward selects and permutes in one launch (each of its 16
 // waves selects at most one token; beyond, two launches are faster)
-constexpr int64_t SELECT_PERMUTE_MAX_TOKENS = 4;
+constexpr int64_t SELECT_PERMUTE_MAX_TOKENS = 16;
 constexpr size_t ALIGN = 256;
 
 size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }

@@ -234,38 +234,43 @@ __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p
   permute_small(p);
 }
 
-// Decode-sized calls: the grouped top-k of every token from its logits (each
-// wave takes tokens w, w + 4, ...) and then the permute of their slots, in
-// one launch.  The selection is route.hip's, so the routing is the same; the
-// barrier makes each wave's topk_idx visible to the permute.
-static_assert(PM_THREADS >= RT_MAXE, "one thread per expert stages the bias");
-__global__ __launch_bounds__(PM_THREADS) void select_permute_kernel(RouteArgs r, PermuteArgs p) {
+// Decode-sized calls: the grouped top-k of every token from its logits (16
+// waves, each taking tokens w, w + 16, ...) and then the permute of their
+// slots, in one launch.  The selection is route.hip's, so the routing is the
+// same; the barrier makes each wave's topk_idx visible to the permute, which
+// runs on the first PM_THREADS threads while the other waves end (a barrier
+// waits only for the waves of the workgroup that have not ended).
+constexpr int SP_THREADS = 1024;
+constexpr int SP_WAVES = SP_THREADS / WAVE;
+static_assert(SP_THREADS >= RT_MAXE, "one thread per expert stages the bias");
+__global__ __launch_bounds__(SP_THREADS) void select_permute_kernel(RouteArgs r, PermuteArgs p) {
   __shared__ f32x4_t lds_l[SP_MAX_LOGITS / 4];
   __shared__ float lds_b[RT_MAXE];
-  __shared__ SelScratch scr[PM_WAVES];
+  __shared__ SelScratch scr[SP_WAVES];
   // every token's logits and the correction bias into LDS, all loads in
   // flight together
   const int n4 = static_cast<int>(r.tokens) * r.n_experts / 4;
-  constexpr int PER = SP_MAX_LOGITS / 4 / PM_THREADS;
+  constexpr int PER = SP_MAX_LOGITS / 4 / SP_THREADS;
   f32x4_t v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = u * PM_THREADS + threadIdx.x;
+    const int i = u * SP_THREADS + threadIdx.x;
     if (i < n4) v[u] = reinterpret_cast<const f32x4_t*>(r.logits)[i];
   }
   const float bias = threadIdx.x < r.n_experts ? r.e_bias[threadIdx.x] : 0.0f;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
-    const int i = u * PM_THREADS + threadIdx.x;
+    const int i = u * SP_THREADS + threadIdx.x;
     if (i < n4) lds_l[i] = v[u];
   }
   if (threadIdx.x < r.n_experts) lds_b[threadIdx.x] = bias;
   __syncthreads();
   const int wave = threadIdx.x / WAVE;
   const float* logits = reinterpret_cast<const float*>(lds_l);
-  for (int64_t t = wave; t < r.tokens; t += PM_WAVES)
+  for (int64_t t = wave; t < r.tokens; t += SP_WAVES)
     select_one(r, logits + t * r.n_experts, t, scr[wave], lds_b);
   __syncthreads();
+  if (threadIdx.x >= PM_THREADS) return;
   permute_small(p);
 }
 
@@ -507,7 +512,7 @@ hipError_t launch_permute(const PermuteArgs& p, hipStream_t stream, Timing t) {
 hipError_t launch_select_permute(const RouteArgs& r, const PermuteArgs& p, hipStream_t stream,
                                  Timing t) {
   if (p.slots <= 0) return hipSuccess;
-  return launch_k(select_permute_kernel, dim3(1), dim3(PM_THREADS), stream, t, r, p);
+  return launch_k(select_permute_kernel, dim3(1), dim3(SP_THREADS), stream, t, r, p);
 }
 
 hipError_t launch_gather(const GatherArgs& p, hipStream_t stream) {

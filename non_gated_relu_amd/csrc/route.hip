@@ -30,7 +30,7 @@ namespace {
 constexpr int RT_TOK = 16;     // tokens per block
 constexpr int RT_WAVES = 8;    // waves of route_kernel
 constexpr int ROUTE_U = 8;     // K steps in flight per wave (route_kernel)
-constexpr int LOGIT_U = 21;    // K steps in flight per wave (route_logits_kernel)
+constexpr int LOGIT_U = 28;    // K steps in flight per wave (route_logits_kernel)
 
 // Logits of 16 tokens x 16 experts: lane holds expert row, tokens 4*grp..+3.
 template <int KIND, int U>
