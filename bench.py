@@ -13,7 +13,10 @@ in 8 groups, top-6 from one group, I=1856, shared 3712, bf16, eight experts'
 correction bias raised by 2.0).  Besides tokens/s the line carries the
 roofline of the dominant kernel, timed live with per-kernel HIP events on the
 stream the kernels run on, and the fp64 CPU oracle timed on a bounded sample
-of the same workload (its first 1024 tokens at most).
+of the same workload (its first 1024 tokens at most).  After the default
+workload, the line's ``other_workloads`` gives the same timing, in short, for
+the decode step (T=32, bf16 and 4-bit experts), the balanced prefill chunk
+(T=4096) and the fp8 experts (T=8192); ``--no-others`` skips them.
 """
 
 from __future__ import annotations
@@ -37,6 +40,10 @@ DEFAULT_WORKLOAD = "skew-bf16-T16384"
 DEFAULT_STEPS = {"tiny-f32-T64": 200, "decode-bf16-T32": 200, "prefill-bf16-T4096": 50,
                  "skew-bf16-T16384": 20, "fp8-T8192": 30, "decode-fp4-T32": 200,
                  "block-decode-bf16-T32": 200}
+# configurations timed after the default one (steps each), reported in short
+OTHER_WORKLOADS = ["decode-bf16-T32", "prefill-bf16-T4096", "fp8-T8192", "decode-fp4-T32"]
+OTHER_STEPS = {"decode-bf16-T32": 100, "prefill-bf16-T4096": 30, "fp8-T8192": 20,
+               "decode-fp4-T32": 100}
 # tokens of the oracle's timed sample (about 12 s of fp64 work on 16 host threads)
 CPU_SAMPLE_TOKENS = 1024
 # kernels whose counter readings are reported as "traffic"
@@ -200,55 +207,17 @@ def cpu_baseline(wl, inp, y_gpu, idx_gpu, budget_s: float):
     return base, parity
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="run the workload at this many tokens instead (a prefix of its rows)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="wall time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches only (default: the step replayed from a HIP graph)")
-    ap.add_argument("--evict-mb", type=int, default=512,
-                    help="after the timed region, repeat the eager steps with a read of this "
-                         "many MB between them (outside their events), so that nothing of one "
-                         "step stays in the 256 MB Infinity Cache for the next (0 = skip)")
-    ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="only run 10 device-to-device copies of this many bytes (a "
-                         "reference kernel for calibrating HBM byte counters)")
-    args = ap.parse_args()
-    if args.copy_bytes:
-        import torch
-        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(10):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 10}))
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(wl, steps: int, warmup: int, graph: bool, evict_mb: int):
+    """Time `steps` layer steps of workload `wl` (after `warmup` untimed ones):
+    per-kernel HIP events on the eager steps, then the whole step replayed
+    from a HIP graph.  Returns the figures, and the layer, its input and its
+    output for the oracle check."""
     import numpy as np
     import torch
 
     from non_gated_relu_amd import binding
-    from non_gated_relu_amd.synthetic import WORKLOADS, make_inputs
+    from non_gated_relu_amd.synthetic import make_inputs
 
-    wl = WORKLOADS[args.workload]
-    steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
-    if args.tokens > 0:
-        wl = dataclasses.replace(wl, tokens=args.tokens,
-                                 name=re.sub(r"T\d+$", f"T{args.tokens}", wl.name))
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
     dev = torch.device("cuda:0")
     print(f"bench: generating {wl.name}", file=sys.stderr, flush=True)
     inp = make_inputs(wl)
@@ -266,8 +235,8 @@ def main():
     # one set of kernel timestamp events per timed step, read after the region
     evs = [binding.StageEvents() for _ in range(steps)]
 
-    print(f"bench: warmup {args.warmup}, timing {steps} steps", file=sys.stderr, flush=True)
-    for i in range(args.warmup):
+    print(f"bench: warmup {warmup}, timing {steps} steps", file=sys.stderr, flush=True)
+    for i in range(warmup):
         run(evs[i % steps])
     torch.cuda.synchronize()
 
@@ -290,9 +259,9 @@ def main():
 
     # the same step replayed from a HIP graph: no per-kernel launch gaps
     graph_s = None
-    if not args.no_graph:
+    if graph:
         gstep = binding.GraphStep(layer, x, y, block=block)
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             gstep.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -305,8 +274,8 @@ def main():
     # cache check: the eager steps again, each after reading a buffer larger than
     # the Infinity Cache (a read, so no dirty lines are left to write back)
     cache_check = None
-    if args.evict_mb > 0:
-        big = torch.ones(args.evict_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    if evict_mb > 0:
+        big = torch.ones(evict_mb * (1 << 20) // 4, dtype=torch.float32, device=dev)
         sink = torch.zeros((), dtype=torch.float32, device=dev)
         evs2 = [binding.StageEvents() for _ in range(steps)]
         for i in range(steps):
@@ -317,7 +286,7 @@ def main():
         for e in evs2:
             for s, ms in e.elapsed_ms(stages).items():
                 ev_stage[s] += ms / steps
-        cache_check = {"evict": f"{args.evict_mb} MB read before each eager step",
+        cache_check = {"evict": f"{evict_mb} MB read before each eager step",
                        "stages_ms_sum": round(sum(stage_ms.values()), 5),
                        "stages_ms_sum_after_evict": round(sum(ev_stage.values()), 5)}
         del big
@@ -359,31 +328,124 @@ def main():
                  "algorithmic_flops_per_step": flops, "algorithmic_bytes_per_step": byts,
                  "active_experts": active}
 
-    line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
-            "steps": steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+    fig = {"value": tokens_per_s, "ms_per_step": ms_per_step,
+           "launch": ("hipGraph replay of " if graph_s else "eager ") +
+                     ("moe_block_forward" if block else "moe_forward"),
+           "eager_ms_per_step": 1e3 * eager_s / steps,
+           "eager_kernel_ms_per_step": {"p10": round(float(q10), 5),
+                                        "median": round(float(q50), 5),
+                                        "p90": round(float(q90), 5)},
+           "roofline": roofline, "layer": layer_fig,
+           "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
+    if cache_check:
+        fig["cache_check"] = cache_check
+    return fig, layer, inp, y
+
+
+def wl_dtype(wl):
+    return {"fp8": "fp8+bf16", "fp4": "bf16 (fp4 weights)"}.get(wl.expert_dtype, wl.act_dtype)
+
+
+def brief(wl, fig, steps: int):
+    """A workload's figures in short, for the line's `other_workloads`."""
+    r = fig["roofline"]
+    lay = fig["layer"]
+    return {"tokens": wl.tokens, "expert_dtype": wl.expert_dtype, "steps": steps,
+            "ms_per_step": round(fig["ms_per_step"], 5),
+            "tokens_per_s": round(fig["value"], 1), "launch": fig["launch"],
+            "layer_tflops_frac_bf16_peak": round(lay["tflops_frac_bf16_peak"], 4),
+            "layer_hbm_frac": round(lay["hbm_frac"], 4),
+            "roofline": {"bound": r["bound"], "kernel": r["kernel"],
+                         "kernel_ms": round(r["kernel_ms"], 5),
+                         "achieved": round(r["achieved"], 1), "peak": r["peak"],
+                         "unit": r["unit"], "frac": round(r["frac"], 4),
+                         "traffic": r["traffic"]},
+            "stages_ms": fig["stages_ms"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload at this many tokens instead (a prefix of its rows)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (default: the step replayed from a HIP graph)")
+    ap.add_argument("--evict-mb", type=int, default=512,
+                    help="after the timed region, repeat the eager steps with a read of this "
+                         "many MB between them (outside their events), so that nothing of one "
+                         "step stays in the 256 MB Infinity Cache for the next (0 = skip)")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="with the default workload, skip timing the other configurations "
+                         "after it")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run 10 device-to-device copies of this many bytes (a "
+                         "reference kernel for calibrating HBM byte counters)")
+    args = ap.parse_args()
+    if args.copy_bytes:
+        import torch
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4, "copies": 10}))
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from non_gated_relu_amd.synthetic import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    steps = args.steps or DEFAULT_STEPS.get(args.workload, 50)
+    if args.tokens > 0:
+        wl = dataclasses.replace(wl, tokens=args.tokens,
+                                 name=re.sub(r"T\d+$", f"T{args.tokens}", wl.name))
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    fig, layer, inp, y = measure(wl, steps, args.warmup, not args.no_graph, args.evict_mb)
+
+    line = {"metric": METRIC, "value": fig["value"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": steps, "warmup": args.warmup, "ms_per_step": fig["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": {"fp8": "fp8+bf16", "fp4": "bf16 (fp4 weights)"}.get(wl.expert_dtype,
-                                                                         wl.act_dtype),
+            "dtype": wl_dtype(wl),
             "data": "synthetic (seeded Gaussian inputs and weights)",
             "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,
                        "experts": wl.n_experts, "groups": wl.n_group,
                        "topk_group": wl.topk_group, "top_k": wl.top_k, "inter": wl.inter,
                        "shared_inter": wl.shared_inter, "expert_dtype": wl.expert_dtype,
-                       "parallelism": "single GPU"},
-            "launch": ("hipGraph replay of " if graph_s else "eager ") +
-                      ("moe_block_forward" if block else "moe_forward"),
-            "eager_ms_per_step": 1e3 * eager_s / steps,
-            "eager_kernel_ms_per_step": {"p10": round(float(q10), 5), "median": round(float(q50), 5),
-                                         "p90": round(float(q90), 5)},
-            "roofline": roofline, "layer": layer_fig,
-            "stages_ms": {s: round(v, 5) for s, v in stage_ms.items()}}
-    if cache_check:
-        line["cache_check"] = cache_check
+                       "parallelism": "single GPU"}}
+    line.update({k: v for k, v in fig.items() if k not in ("value", "ms_per_step")})
     if args.cpu_seconds > 0:
         y_np = y.float().cpu().numpy()
         idx_np = layer.topk_idx[:wl.tokens].cpu().numpy()
         line["cpu_baseline"], line["parity"] = cpu_baseline(wl, inp, y_np, idx_np,
                                                             args.cpu_seconds)
+    if args.others and args.workload == DEFAULT_WORKLOAD and args.tokens == 0:
+        # the other one-GPU configurations, timed the same way after the
+        # headline (their oracle parity is in the tests): the decode steps
+        # that stream the expert weights, the balanced prefill chunk, the fp8
+        # experts and the 4-bit decode step
+        del layer, inp, y
+        torch.cuda.empty_cache()
+        line["other_workloads"] = {}
+        for name in OTHER_WORKLOADS:
+            owl = WORKLOADS[name]
+            ost = OTHER_STEPS[name]
+            ofig, olayer, _, _ = measure(owl, ost, min(args.warmup, 5), not args.no_graph, 0)
+            line["other_workloads"][name] = brief(owl, ofig, ost)
+            del olayer
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 
