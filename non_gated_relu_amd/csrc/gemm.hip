@@ -412,7 +412,10 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
   if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
   const GemmProblem& p = t.p;
-  const int wave = threadIdx.x / WAVE;
+  // (the wave index through readfirstlane: the compiler then knows it, and all
+  // that derives from it, to be the same on every lane of the wave, so tests
+  // on it are scalar branches instead of per-lane exec masks)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int lane = lane_id();
   const int64_t kbytes = int64_t(p.k) * KindTraits<KIND>::ESZ;
   const int nk = static_cast<int>(kbytes / RG_ROWB);  // the host guarantees K bytes % 64 == 0
@@ -525,15 +528,15 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
 
   // Fragment reads and MFMAs of one stage, in four quarters: quarter q reads
   // B fragments [q FN/4, (q+1) FN/4) and A fragments 2q, 2q + 1, and does the
-  // MFMAs of A rows 2q, 2q + 1 (FMV row fragments in all; all columns when
-  // FULL_N, else the first fn_valid column fragments).
+  // MFMAs of A rows 2q, 2q + 1 (FMV row fragments in all; the first FNV
+  // column fragments, or the first fn_valid when FNV is -1).
   auto load_quarter = [&](int q, const char* buf, i32x4_t (&af)[FM], i32x4_t (&bf)[FN],
                           auto fmv_c, auto full_c) {
     constexpr int FMV = decltype(fmv_c)::value;
-    constexpr bool FULL_N = decltype(full_c)::value;
+    constexpr int FNV = decltype(full_c)::value;
 #pragma unroll
     for (int j = q * (FN / QUARTERS); j < (q + 1) * (FN / QUARTERS); ++j)
-      if (FULL_N || j < fn_valid)
+      if (FNV >= 0 ? j < FNV : j < fn_valid)
         bf[j] = *reinterpret_cast<const i32x4_t*>(buf + RG_ABYTES + (wn + WN * j) * 1024 + lofs);
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i)
@@ -542,12 +545,13 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   auto mma_quarter = [&](int q, const i32x4_t (&af)[FM], const i32x4_t (&bf)[FN], auto fmv_c,
                          auto full_c) {
     constexpr int FMV = decltype(fmv_c)::value;
-    constexpr bool FULL_N = decltype(full_c)::value;
+    constexpr int FNV = decltype(full_c)::value;
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        if (i < FMV && (FULL_N || j < fn_valid)) acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
+        if (i < FMV && (FNV >= 0 ? j < FNV : j < fn_valid))
+          acc[i][j] = mfma_bf16(bf[j], af[i], acc[i][j]);
   };
 
   // Stage s lives in ring slot s % RING and is fetched RING - 1 stages ahead.
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   // so the last step adds exact zeros.
   auto k_loop_fp8 = [&](auto fmv_c, auto full_c) {
     constexpr int FMV = decltype(fmv_c)::value;
-    constexpr bool FULL_N = decltype(full_c)::value;
+    constexpr int FNV = decltype(full_c)::value;
     constexpr int HALF = RG_ABYTES;  // one stage of one operand
     char* const a_region = ring;             // 2 slots
     char* const b_region = ring + 4 * HALF;  // 3 slots
@@ -671,14 +675,14 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       i32x8_t af[FM], bf[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        if (FULL_N || j < fn_valid) bf[j] = frag(cb + (wn + WN * j) * 1024);
+        if (FNV >= 0 ? j < FNV : j < fn_valid) bf[j] = frag(cb + (wn + WN * j) * 1024);
 #pragma unroll
       for (int i = 0; i < FMV; ++i) af[i] = frag(ca + (wm + WM * i) * 1024);
 #pragma unroll
       for (int i = 0; i < FMV / 2; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
+          if (FNV >= 0 ? j < FNV : j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
       // the weights of step u + 2 between the two halves of the MFMAs: the
       // fragment reads go first, and the fetches have two steps to land
       __builtin_amdgcn_sched_barrier(0);
@@ -688,7 +692,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       for (int i = FMV / 2; i < FMV; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          if (FULL_N || j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
+          if (FNV >= 0 ? j < FNV : j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
     }
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   };
@@ -707,11 +711,19 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       default: loop(std::integral_constant<I, 0>{}, full_c); break;
     }
   };
+  // The loop instance also fixes the wave's count of valid column fragments
+  // when it is FN, 2 or 1 (the last N tile of N = 1856, 2688 or 3712 leaves
+  // each wave one or two); other counts test it at run time.
   auto run = [&](auto& loop) {
-    if (full_n)
-      with_rows(loop, std::true_type{});
+    using I = int;
+    if (full_n || fn_valid == FN)
+      with_rows(loop, std::integral_constant<I, FN>{});
+    else if (fn_valid == 2)
+      with_rows(loop, std::integral_constant<I, 2>{});
+    else if (fn_valid == 1)
+      with_rows(loop, std::integral_constant<I, 1>{});
     else
-      with_rows(loop, std::false_type{});
+      with_rows(loop, std::integral_constant<I, -1>{});
   };
   if constexpr (KIND == K_FP8) {
     run(k_loop_fp8);
