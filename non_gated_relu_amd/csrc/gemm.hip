@@ -462,6 +462,18 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       src[q] = wbase + int64_t(n) * kbytes + chunk * 16;
     }
   }
+  // fp8: the fetch sources again, as a uniform base plus a 32-bit lane offset
+  // (the host keeps a_rows K and N K below 2^32 for this kernel), which the
+  // main K steps advance with scalar adds only
+  const char* const a_base = static_cast<const char*>(p.a);
+  uint32_t a_off[2] = {0, 0}, w_off[2] = {0, 0};
+  if constexpr (KIND == K_FP8) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a_off[q] = static_cast<uint32_t>(src[q] - a_base);
+      w_off[q] = static_cast<uint32_t>(src[q + 2] - wbase);
+    }
+  }
   int dma_on = 0;  // bit q: block wave + NW q is fetched (set with the tile's extent below)
   auto dma_one = [&](int q, int s, char* buf) {
     const int64_t kb = int64_t(min(s, nk - 1)) * RG_ROWB;  // past the end: harmless re-read
@@ -507,15 +519,17 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   const int nblk = (min(p.n - t.n0, RG_BN) + 15) / 16;
   const int fn_valid = min(max((nblk - wn + WN - 1) / WN, 0), FN);
   const bool full_n = nblk * 16 >= RG_BN;
-  // fp8: the DMA skips 16-row blocks wholly past the group end (A) or past N
-  // (B); only skipped fragments would read them, and the fp8 K loop waits for
-  // all its fetches (vmcnt 0), whatever their number.  (The bf16 loop's waits
-  // count its fetches; skipping there measured 4-7% slower.)
+  // fp8: the DMA skips 16-row blocks of activation rows wholly past the group
+  // end; only skipped fragments would read them, and they are fetched before
+  // the weight rows, which the waits count.  Weight blocks past N are fetched
+  // (their rows clamped to N - 1), so every wave has four weight fetches per
+  // step.  (The bf16 loop's waits count all its fetches; skipping there
+  // measured 4-7% slower.)
   if constexpr (KIND == K_FP8) {
 #pragma unroll
     for (int q = 0; q < DMA_PER_WAVE; ++q) {
       const int blk = wave + NW * q;
-      const bool on = blk < 16 ? blk < mblk : blk - 16 < nblk;
+      const bool on = blk < 16 ? blk < mblk : true;
       dma_on |= on ? 1 << q : 0;
     }
   }
@@ -650,28 +664,22 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       fill_half(2 * u, b, 2);
       fill_half(2 * u + 1, b + HALF, 2);
     };
-    // this wave's weight fetches per step (blocks q = 2, 3 of both stages)
-    const int nb = 2 * (((dma_on >> 2) & 1) + ((dma_on >> 3) & 1));
     const int nsteps = (nk + 1) / 2;
-    fill_a(0);
-    fill_b(0);
-    if (nsteps > 1) fill_b(1);
-    for (int u = 0; u < nsteps; ++u) {
-      // this wave's fetches of step u (issued before those of the weights of
-      // step u + 1) have landed and its reads of step u - 1 are done; after
-      // the barrier the same holds for all waves.  The weights of step u + 1
-      // may still fly when both their stages are fetches.
-      const bool relaxed = 2 * u + 3 < nk;
-      if (relaxed && nb == 4)
+    // one step: wait, barrier, the activation rows of step u + 1, the
+    // fragment reads and first half of the MFMAs, the weight rows of step
+    // u + 2, the second half.  `wait_step` waits for this wave's fetches of
+    // step u (and its reads of step u - 1); the weights of step u + 1, this
+    // wave's four youngest fetches, may still fly when `relaxed`.  `fa` and
+    // `fb` issue the fetches; a_slot and b_slot are the step's LDS slots.
+    auto step = [&](int u, bool relaxed, int a_slot, int b_slot, auto fa, auto fb) {
+      if (relaxed)
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
-      else if (relaxed && nb == 2)
-        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2, 0));
       else
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
       block_sync_lds();
-      if (u + 1 < nsteps) fill_a(u + 1);
-      const char* ca = a_region + (u & 1) * 2 * HALF + (lgrp >> 1) * HALF;
-      const char* cb = b_region + (u % 3) * 2 * HALF + (lgrp >> 1) * HALF;
+      fa(u + 1);
+      const char* ca = a_region + a_slot * 2 * HALF + (lgrp >> 1) * HALF;
+      const char* cb = b_region + b_slot * 2 * HALF + (lgrp >> 1) * HALF;
       i32x8_t af[FM], bf[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
@@ -686,13 +694,65 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       // the weights of step u + 2 between the two halves of the MFMAs: the
       // fragment reads go first, and the fetches have two steps to land
       __builtin_amdgcn_sched_barrier(0);
-      if (u + 2 < nsteps) fill_b(u + 2);
+      fb(u + 2);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = FMV / 2; i < FMV; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           if (FNV >= 0 ? j < FNV : j < fn_valid) acc[i][j] = mfma_fp8(bf[j], af[i], acc[i][j]);
+    };
+    fill_a(0);
+    fill_b(0);
+    if (nsteps > 1) fill_b(1);
+    // Main steps: every fetch they issue (stages 2u + 2 .. 2u + 5) lies
+    // inside K, so they fetch without tests; the fetch sources advance from
+    // uniform bases (addresses of one scalar base and a 32-bit lane offset),
+    // and the slots rotate in scalar registers.
+    const int u_main = max((nk - 4) / 2, 0);
+    int a_slot = 0, b_slot = 0;
+    int u = 0;
+    for (; u < u_main; ++u) {
+      const int a_next = a_slot ^ 1;
+      const int b_next2 = b_slot == 0 ? 2 : b_slot - 1;  // (u + 2) % 3
+      step(u, true, a_slot, b_slot,
+           [&](int v) {
+             char* dst = a_region + a_next * 2 * HALF;
+             const char* from = a_base + int64_t(2 * v) * RG_ROWB;
+#pragma unroll
+             for (int h = 0; h < 2; ++h)
+#pragma unroll
+               for (int q = 0; q < 2; ++q)
+                 if (dma_on & (1 << q))
+                   __builtin_amdgcn_global_load_lds(from + h * RG_ROWB + a_off[q],
+                                                    MOE_LDS_PTR(dst + h * HALF +
+                                                                (wave + NW * q) * 1024),
+                                                    16, 0, 0);
+           },
+           [&](int v) {
+             char* dst = b_region + b_next2 * 2 * HALF - HALF;  // weight blocks are 16..31
+             const char* from = wbase + int64_t(2 * v) * RG_ROWB;
+#pragma unroll
+             for (int h = 0; h < 2; ++h)
+#pragma unroll
+               for (int q = 0; q < 2; ++q)
+                 __builtin_amdgcn_global_load_lds(from + h * RG_ROWB + w_off[q],
+                                                  MOE_LDS_PTR(dst + h * HALF +
+                                                              (wave + NW * (q + 2)) * 1024),
+                                                  16, 0, 0);
+           });
+      a_slot = a_next;
+      b_slot = b_slot == 2 ? 0 : b_slot + 1;
+    }
+    // The last steps: fetches past the end of K zero-fill their stage.
+    for (; u < nsteps; ++u) {
+      step(u, 2 * u + 3 < nk, u & 1, u % 3,
+           [&](int v) {
+             if (v < nsteps) fill_a(v);
+           },
+           [&](int v) {
+             if (v < nsteps) fill_b(v);
+           });
     }
     __builtin_amdgcn_s_waitcnt(WAIT_VM0);
   };
@@ -1342,7 +1402,11 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
       return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
   }
   if constexpr (KIND == K_FP8) {
-    if (shape.bm == RG_BM)
+    // (the ring kernel addresses fp8 rows by 32-bit offsets)
+    auto fits = [](const GemmProblem& q) {
+      return !q.w || (q.a_rows * q.k < (int64_t(1) << 32) && int64_t(q.n) * q.k < (int64_t(1) << 32));
+    };
+    if (shape.bm == RG_BM && fits(p.prob[0]) && fits(p.prob[1]))
       return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
   }
   // two workgroups per CU: 64 tiles per XCD in flight
