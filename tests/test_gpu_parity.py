@@ -35,6 +35,13 @@ BIG_GROUPS_BF16 = Workload("big-groups-bf16-T1024", 1024, 256, 16, 4, 1, 2, 320,
 BIG_GROUPS_FP8 = Workload("big-groups-fp8-T1024", 1024, 256, 16, 4, 1, 2, 320, 192, "bf16", "fp8",
                           seed=28)
 SHORT_K = Workload("big-groups-bf16-d64", 1024, 64, 16, 4, 1, 2, 128, 64, "bf16", "bf16", seed=29)
+# fp8 K loops with 6 to 9 ring stages (K = 384 .. 576 bytes): the first
+# lengths where main steps (all fetches inside K) run before the last steps,
+# with an even and an odd stage count in each projection
+RING_FP8_K7 = Workload("big-groups-fp8-d448", 1024, 448, 16, 4, 1, 2, 384, 0, "bf16", "fp8",
+                       seed=35)
+RING_FP8_K9 = Workload("big-groups-fp8-d576", 1024, 576, 16, 4, 1, 2, 512, 0, "bf16", "fp8",
+                       seed=36)
 # 4-bit experts: K = 192 and 320 end in half a 128-element super-block; the
 # shared expert is fp4 (one launch with the routed experts) or bf16 (its own).
 RAGGED_FP4 = Workload("ragged-fp4-T77", 77, 256, 32, 4, 2, 4, 192, 320, "bf16", "fp4", seed=30,
@@ -333,8 +340,8 @@ def test_graph_replays_match_eager(wl):
     del other
 
 
-@pytest.mark.parametrize("wl", [BIG_GROUPS_BF16, BIG_GROUPS_FP8, BIG_GROUPS_FP4],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [BIG_GROUPS_BF16, BIG_GROUPS_FP8, BIG_GROUPS_FP4, RING_FP8_K7,
+                                RING_FP8_K9], ids=lambda w: w.name)
 def test_expert_rows_do_not_depend_on_the_tile_shape(wl):
     """A row's result is the same whichever tile shape computes it: a call
     with hundreds of rows per expert (256-row tiles) and a call with a few
