@@ -667,10 +667,10 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
     const int nsteps = (nk + 1) / 2;
     // one step: wait, barrier, the activation rows of step u + 1, the
     // fragment reads and first half of the MFMAs, the weight rows of step
-    // u + 2, the second half.  `wait_step` waits for this wave's fetches of
-    // step u (and its reads of step u - 1); the weights of step u + 1, this
-    // wave's four youngest fetches, may still fly when `relaxed`.  `fa` and
-    // `fb` issue the fetches; a_slot and b_slot are the step's LDS slots.
+    // u + 2, the second half.  The wait is for this wave's fetches of step u
+    // (and its reads of step u - 1); the weights of step u + 1, this wave's
+    // four youngest fetches, may still fly when `relaxed`.  `fa` and `fb`
+    // issue the fetches; a_slot and b_slot are the step's LDS slots.
     auto step = [&](int u, bool relaxed, int a_slot, int b_slot, auto fa, auto fb) {
       if (relaxed)
         __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
