@@ -230,6 +230,92 @@ __device__ __forceinline__ void permute_small(const PermuteArgs& p) {
   place_chunk(ids, 0, n, E, run, wc, p.sorted_slot, p.slot_pos);
 }
 
+// The same outputs from one wave, for at most 64 slots (one per lane) and
+// 256 experts, without a workgroup barrier: a lane's slot finds the slots of
+// its expert with ballots (match_key), the first of them scatters the count,
+// and the experts' counts, offsets and tile counts are scanned across the
+// wave with shuffles, expert x = lane + 64 j in ascending order.
+constexpr int PW_MAX_SLOTS = WAVE;
+__device__ void permute_wave(const PermuteArgs& p) {
+  __shared__ int32_t cnt[RT_MAXE];
+  __shared__ int32_t off[RT_MAXE];
+  const int lane = lane_id();
+  const int E = p.n_experts;
+  const int S = static_cast<int>(p.slots);
+  const bool valid = lane < S;
+  const int e = valid ? min(max(p.topk_idx[lane], 0), E - 1) : 0;
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j)
+    if (lane + WAVE * j < E) cnt[lane + WAVE * j] = 0;
+  const uint64_t m = match_key(valid ? (uint32_t(e) | 0x200u) : 0u);
+  const int rank = __popcll(m & lanemask_lt());
+  wave_lds_sync();
+  if (valid && rank == 0) cnt[e] = __popcll(m);
+  wave_lds_sync();
+  // per expert: count, exclusive offset, tile count and first tile
+  const ScheduleSpec& sp = p.sched;
+  int32_t c[RT_EPL], o[RT_EPL], nt[RT_EPL], t0[RT_EPL];
+  int32_t carry = 0, tcarry = 0;
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int x = lane + WAVE * j;
+    c[j] = x < E ? cnt[x] : 0;
+    nt[j] = c[j] > 0 && sp.sched ? (c[j] + sp.bm - 1) / sp.bm : 0;
+    int32_t ic = c[j], it = nt[j];  // inclusive scans over the wave's lanes
+#pragma unroll
+    for (int d = 1; d < WAVE; d <<= 1) {
+      const int32_t uc = __shfl_up(ic, d), ut = __shfl_up(it, d);
+      if (lane >= d) {
+        ic += uc;
+        it += ut;
+      }
+    }
+    o[j] = carry + ic - c[j];
+    t0[j] = tcarry + it - nt[j];
+    carry += __shfl(ic, WAVE - 1);
+    tcarry += __shfl(it, WAVE - 1);
+    if (x < E) {
+      p.expert_counts[x] = c[j];
+      p.expert_offsets[x] = o[j];
+      off[x] = o[j];
+    }
+  }
+  if (lane == 0) p.expert_offsets[E] = S;
+  wave_lds_sync();
+  if (valid) {
+    const int pos = off[e] + rank;
+    p.sorted_slot[pos] = lane;
+    p.slot_pos[lane] = pos;
+  }
+  if (!sp.sched) return;
+  // the schedule: each expert's tiles, groups in order, then the extra group
+#pragma unroll
+  for (int j = 0; j < RT_EPL; ++j) {
+    const int x = lane + WAVE * j;
+    for (int q = 0; q < nt[j]; ++q) {
+      const int32_t at = t0[j] + q;
+      if (at < sp.max_tiles) {
+        sp.sched[2 + 2 * at] = x | (min(sp.bm, c[j] - q * sp.bm) << 16);
+        sp.sched[3 + 2 * at] = o[j] + q * sp.bm;
+      }
+    }
+  }
+  const int32_t extra =
+      sp.extra_rows > 0 ? static_cast<int32_t>((sp.extra_rows + sp.bm - 1) / sp.bm) : 0;
+  for (int q = lane; q < extra; q += WAVE) {
+    const int32_t at = tcarry + q;
+    if (at < sp.max_tiles) {
+      const int32_t rows = static_cast<int32_t>(min<int64_t>(sp.bm, sp.extra_rows - int64_t(q) * sp.bm));
+      sp.sched[2 + 2 * at] = E | (rows << 16);
+      sp.sched[3 + 2 * at] = q * sp.bm;
+    }
+  }
+  if (lane == 0) {
+    sp.sched[0] = min(tcarry + extra, sp.max_tiles);
+    sp.sched[1] = min(tcarry, sp.max_tiles);
+  }
+}
+
 __global__ __launch_bounds__(PM_THREADS) void permute_small_kernel(PermuteArgs p) {
   permute_small(p);
 }
@@ -270,6 +356,11 @@ __global__ __launch_bounds__(SP_THREADS) void select_permute_kernel(RouteArgs r,
   for (int64_t t = wave; t < r.tokens; t += SP_WAVES)
     select_one(r, logits + t * r.n_experts, t, scr[wave], lds_b);
   __syncthreads();
+  if (p.slots <= PW_MAX_SLOTS) {  // (E <= RT_MAXE here)
+    if (threadIdx.x >= WAVE) return;
+    permute_wave(p);
+    return;
+  }
   if (threadIdx.x >= PM_THREADS) return;
   permute_small(p);
 }
