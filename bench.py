@@ -68,6 +68,13 @@ def mfma_dtype(dt):
     return "bf16" if dt == "fp4" else dt
 
 
+def add_flops(stage, dtype, flops):
+    """Record the MFMA work of a launch by operand type (a launch with fp8
+    routed experts and a bf16 shared expert holds both)."""
+    by = stage.setdefault("flops_by_dtype", {stage["dtype"]: stage["flops"] - flops})
+    by[dtype] = by.get(dtype, 0) + flops
+
+
 def stage_work(wl, active: int, stages):
     """Algorithmic bytes and flops of each stage's launch(es) for one step,
     for the stages the library runs (binding.stages_of).
@@ -123,12 +130,14 @@ def stage_work(wl, active: int, stages):
             w["routed_up"]["flops"] += 2 * T * d * Is
             w["routed_up"]["implementation_bytes"] += T * Is * sh_h
             w["routed_up"]["shared_weight_bytes"] = su
+            add_flops(w["routed_up"], mfma_dtype(sdt), 2 * T * d * Is)
         if "shared_down" in stages:
             w["shared_down"] = shared_down
         else:  # one more group of the routed down launch
             for key in ("bytes", "flops", "implementation_bytes"):
                 w["routed_down"][key] += shared_down[key]
             w["routed_down"]["shared_weight_bytes"] = sd
+            add_flops(w["routed_down"], mfma_dtype(sdt), shared_down["flops"])
     if not combined:
         w["combine"] = dict(bytes=y_bytes, flops=0, dtype="f32",
                             implementation_bytes=comb_impl + (T * d * 4 if Is else 0))
@@ -303,6 +312,9 @@ def measure(wl, steps: int, warmup: int, graph: bool, evict_mb: int):
     dw = work[dom]
     t_s = stage_ms[dom] / 1e3
     peak_t = PEAK_TFLOPS[dw["dtype"]]
+    if len(dw.get("flops_by_dtype", {})) > 1:
+        # mixed MFMA types: the rate at which the launch's work would run at each type's peak
+        peak_t = dw["flops"] / sum(f / PEAK_TFLOPS[t] for t, f in dw["flops_by_dtype"].items())
     hbm_bound = dw["bytes"] / (PEAK_HBM_GBS * 1e9) >= dw["flops"] / (peak_t * 1e12)
     if hbm_bound:
         achieved, peak, unit = dw["bytes"] / t_s / 1e9, PEAK_HBM_GBS, "GB/s"
@@ -319,6 +331,9 @@ def measure(wl, steps: int, warmup: int, graph: bool, evict_mb: int):
         roofline["unit_bytes"] = dw["unit_bytes"]
     if "shared_weight_bytes" in dw:
         roofline["shared_weight_bytes_per_launch"] = dw["shared_weight_bytes"]
+    if len(dw.get("flops_by_dtype", {})) > 1:
+        roofline["flops_by_dtype"] = dw["flops_by_dtype"]
+        roofline["peak_note"] = "time-weighted peak of the launch's fp8 and bf16 MFMA work"
 
     flops, byts = layer_work(wl, active)
     layer_fig = {"tflops": flops / total_s * steps / 1e12,

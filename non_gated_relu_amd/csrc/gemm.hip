@@ -391,8 +391,14 @@ __device__ __forceinline__ void block_sync_lds() {
 // NW waves in a 2 x (NW / 2) grid; wave (wm, wn) owns the 16-row blocks
 // wm + 2 i and the 16-column blocks wn + (NW / 2) j of the tile, dealt
 // round-robin so that partial tiles leave every SIMD about the same work.
+template <int KIND, int NW, int RING>
+constexpr int ring_bytes() {
+  return KIND == K_FP8 ? 5 * RG_STAGE : RING * RG_STAGE;
+}
+
+// One 256 x 256 tile `t` of a ring kernel; `ring` is the kernel's LDS ring.
 template <int KIND, int EPI, int NW, int RING>
-__global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
+__device__ __forceinline__ void ring_tile(const Tile& t, char* ring) {
   constexpr int WM = 2, WN = NW / 2;
   constexpr int FM = RG_BM / WM / 16;  // 8
   constexpr int FN = RG_BN / WN / 16;  // 4 (8 waves) or 8 (4 waves)
@@ -404,13 +410,7 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
   static_assert(KIND == K_BF16 ? (RING == 4 || RING == 5) : RING == 4, "ring depth");
   // the ring: RING stages (bf16); for fp8 two activation slots and three
   // weight slots of two stages each, 160 KB
-  constexpr int RING_BYTES = KIND == K_FP8 ? 5 * RG_STAGE : RING * RG_STAGE;
   static_assert(KIND != K_FP8 || NW * WAVE == RG_BM + RG_BN, "one scale per thread");
-  __shared__ __attribute__((aligned(1024))) char ring[RING_BYTES];
-
-  Tile t;
-  const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
-  if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
   const GemmProblem& p = t.p;
   // (the wave index through readfirstlane: the compiler then knows it, and all
   // that derives from it, to be the same on every lane of the wave, so tests
@@ -838,6 +838,34 @@ __global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
       }
     }
   }
+}
+
+template <int KIND, int EPI, int NW, int RING>
+__global__ __launch_bounds__(NW * WAVE) void gemm_ring_kernel(GemmArgs pa) {
+  __shared__ __attribute__((aligned(1024))) char ring[ring_bytes<KIND, NW, RING>()];
+  Tile t;
+  const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
+  if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
+  ring_tile<KIND, EPI, NW, RING>(t, ring);
+}
+
+// fp8 routed experts (prob[0]) and a bf16 shared expert (prob[1]) in one
+// launch: each workgroup runs its tile's kind, so the shared expert's tiles
+// fill the routed ones' last rounds instead of forming a launch of their own.
+// The tiles give the bits of the single-kind kernels.
+template <int EPI>
+__global__ __launch_bounds__(8 * WAVE) void gemm_ring_mixed_kernel(GemmArgs pa) {
+  constexpr int BYTES = ring_bytes<K_FP8, 8, 4>() > ring_bytes<K_BF16, 8, 4>()
+                            ? ring_bytes<K_FP8, 8, 4>()
+                            : ring_bytes<K_BF16, 8, 4>();
+  __shared__ __attribute__((aligned(1024))) char ring[BYTES];
+  Tile t;
+  const int bid = xcd_tile_order(blockIdx.x, gridDim.x, 32);
+  if (!locate_tile<RG_BM, RG_BN>(pa, t, bid)) return;
+  if (t.p.w_scale)  // the fp8 experts carry per-row weight scales
+    ring_tile<K_FP8, EPI, 8, 4>(t, ring);
+  else
+    ring_tile<K_BF16, EPI, 8, 4>(t, ring);
 }
 
 // ---------------------------------------------------------- stream kernel
@@ -1406,8 +1434,12 @@ hipError_t launch_kind_epi(const GemmArgs& p, GemmShape shape, unsigned grid, hi
     auto fits = [](const GemmProblem& q) {
       return !q.w || (q.a_rows * q.k < (int64_t(1) << 32) && int64_t(q.n) * q.k < (int64_t(1) << 32));
     };
-    if (shape.bm == RG_BM && fits(p.prob[0]) && fits(p.prob[1]))
-      return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
+    const bool ring = shape.bm == RG_BM && fits(p.prob[0]) && fits(p.prob[1]);
+    if (p.prob[1].w && !p.prob[1].w_scale) {  // a bf16 second problem: the mixed ring kernel only
+      if (!ring) return hipErrorInvalidValue;
+      return launch_k(gemm_ring_mixed_kernel<EPI>, g, dim3(8 * WAVE), stream, t, p);
+    }
+    if (ring) return launch_k(gemm_ring_kernel<KIND, EPI, 8, 4>, g, dim3(8 * WAVE), stream, t, p);
   }
   // two workgroups per CU: 64 tiles per XCD in flight
   return launch_k(gemm_kernel<KIND, 128, 128, 2, 2, EPI, 256, 64>, g, dim3(256), stream, t, p);

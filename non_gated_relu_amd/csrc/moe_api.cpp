@@ -292,11 +292,27 @@ size_t route_logit_bytes(const moe_config& c, int64_t T) {
   return sizeof(float) * size_t(T) * c.n_experts;
 }
 
+// Whether the shared expert runs as one more group of the routed experts'
+// launches: always when it has their weight type; with fp8 experts and a bf16
+// shared expert when both take the 256 x 256 ring kernels (many rows per
+// expert), whose mixed form runs each tile in its own type, and their rows
+// fit its 32-bit fp8 offsets.
+bool shared_fused(const moe_config& c, int64_t T) {
+  if (c.shared_inter <= 0) return false;
+  if (c.expert_dtype == c.shared_dtype) return true;
+  if (c.expert_dtype != MOE_FP8_E4M3 || c.shared_dtype != MOE_BF16) return false;
+  const int64_t S = T * c.top_k;
+  const int64_t lim = int64_t(1) << 32;
+  return pick_gemm_shape(K_FP8, S, c.n_experts).bm == 256 && T * c.hidden < lim &&
+         S * c.inter < lim && T * c.shared_inter < lim && int64_t(c.inter) * c.hidden < lim &&
+         int64_t(c.shared_inter) * c.hidden < lim;
+}
+
 Forward carve_forward(Carver& cv, const moe_config& c, int64_t T) {
   Forward f;
   f.T = T;
   f.S = T * c.top_k;
-  f.fused_shared = c.shared_inter > 0 && c.expert_dtype == c.shared_dtype;
+  f.fused_shared = shared_fused(c, T);
   if (route_mode(T) != ROUTE_ONE_KERNEL) f.logits = cv.take<float>(route_logit_bytes(c, T));
   f.block_counts = cv.take<int32_t>(sizeof(int32_t) * size_t(permute_chunks(f.S)) * c.n_experts);
   f.topk_idx = cv.take<int32_t>(sizeof(int32_t) * size_t(f.S));
@@ -383,11 +399,11 @@ struct LayerWeights {
 
 // The stages moe_forward runs for a positive token count (bit i: stage i of
 // the MOE_T_* enumeration).
-uint32_t forward_stage_mask(const moe_config& c) {
+uint32_t forward_stage_mask(const moe_config& c, int64_t T) {
   uint32_t m = (1u << MOE_T_ROUTE) | (1u << MOE_T_PERMUTE) | (1u << MOE_T_ROUTED_UP) |
                (1u << MOE_T_ROUTED_DOWN);
   if (c.expert_dtype == MOE_FP8_E4M3) m |= (1u << MOE_T_QUANT_X) | (1u << MOE_T_QUANT_H);
-  const bool own_shared = c.shared_inter > 0 && c.expert_dtype != c.shared_dtype;
+  const bool own_shared = c.shared_inter > 0 && !shared_fused(c, T);
   if (own_shared) m |= (1u << MOE_T_SHARED_UP) | (1u << MOE_T_SHARED_DOWN);
   return m | (1u << MOE_T_COMBINE);
 }
@@ -544,7 +560,7 @@ moe_status moe_forward_stage_mask(const moe_config* cfg, int64_t tokens, uint32_
   if (st != MOE_OK) return st;
   if ((st = check_tokens(cfg, tokens)) != MOE_OK) return st;
   if (!mask) return MOE_ERR_INVALID_ARG;
-  *mask = tokens > 0 ? forward_stage_mask(*cfg) : 0u;
+  *mask = tokens > 0 ? forward_stage_mask(*cfg, tokens) : 0u;
   return MOE_OK;
 }
 
