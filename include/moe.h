@@ -276,10 +276,10 @@ enum {
   MOE_T_ROUTED_DOWN = 5,  /* routed down GEMM                             */
   MOE_T_SHARED_UP = 6,    /* shared-expert up GEMM + relu^2 (its own
                              launch when its weight type differs from the
-                             routed experts')                              */
-  MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM (its own launch when
-                             its weight type differs from the routed
-                             experts')                                     */
+                             routed experts' and the call does not put
+                             both in one launch: moe_forward_stage_mask) */
+  MOE_T_SHARED_DOWN = 7,  /* shared-expert down GEMM (its own launch in
+                             the same cases)                               */
   MOE_T_COMBINE = 8,      /* weighted combine + output rounding           */
   MOE_T_NORM = 9,         /* block only: the RMSNorm before the layer     */
   MOE_T_SLOTS = 10
