@@ -388,15 +388,18 @@ __device__ __forceinline__ void block_sync_lds() {
   __asm__ volatile("" ::: "memory");
 }
 
-// NW waves in a 2 x (NW / 2) grid; wave (wm, wn) owns the 16-row blocks
-// wm + 2 i and the 16-column blocks wn + (NW / 2) j of the tile, dealt
-// round-robin so that partial tiles leave every SIMD about the same work.
+// LDS of a ring kernel: RING stages (bf16); for fp8 two activation slots and
+// three weight slots of two stages each, 160 KB.
 template <int KIND, int NW, int RING>
 constexpr int ring_bytes() {
   return KIND == K_FP8 ? 5 * RG_STAGE : RING * RG_STAGE;
 }
 
-// One 256 x 256 tile `t` of a ring kernel; `ring` is the kernel's LDS ring.
+// One 256 x 256 tile `t` of a ring kernel; `ring` is the kernel's LDS ring
+// (its only __shared__ object).  NW waves in a 2 x (NW / 2) grid; wave
+// (wm, wn) owns the 16-row blocks wm + 2 i and the 16-column blocks
+// wn + (NW / 2) j of the tile, dealt round-robin so that partial tiles leave
+// every SIMD about the same work.
 template <int KIND, int EPI, int NW, int RING>
 __device__ __forceinline__ void ring_tile(const Tile& t, char* ring) {
   constexpr int WM = 2, WN = NW / 2;
@@ -408,8 +411,6 @@ __device__ __forceinline__ void ring_tile(const Tile& t, char* ring) {
   static_assert(DMA_PER_WAVE % QUARTERS == 0 && FN % QUARTERS == 0, "quarter split");
   // (a fifth bf16 slot, 160 KB in all, measured 2-3% slower)
   static_assert(KIND == K_BF16 ? (RING == 4 || RING == 5) : RING == 4, "ring depth");
-  // the ring: RING stages (bf16); for fp8 two activation slots and three
-  // weight slots of two stages each, 160 KB
   static_assert(KIND != K_FP8 || NW * WAVE == RG_BM + RG_BN, "one scale per thread");
   const GemmProblem& p = t.p;
   // (the wave index through readfirstlane: the compiler then knows it, and all
