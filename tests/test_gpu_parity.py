@@ -262,6 +262,42 @@ def test_exact_ties_in_the_forward_selection(wl):
     np.testing.assert_allclose(layer.topk_w[:wl.tokens].cpu().numpy(), 2.5 / wl.top_k, rtol=1e-7)
 
 
+# (E, G, topk_group, top_k) on both selection paths: the register path (a
+# power-of-two group of 1 to 64 experts, at most 64 experts in the kept
+# groups) and the general one (6 or 128 experts per group, or 96 kept); E =
+# 48, 80 and 96 leave the last wave-wide run of experts partly empty.
+SELECT_SHAPES = [(48, 48, 6, 6), (64, 32, 3, 4), (80, 5, 2, 8), (128, 4, 2, 8), (256, 4, 1, 8),
+                 (96, 16, 3, 8), (128, 4, 3, 8), (256, 2, 1, 8)]
+
+
+@pytest.mark.parametrize("E,G,tg,k", SELECT_SHAPES,
+                         ids=[f"E{e}-G{g}-tg{t}-k{k}" for e, g, t, k in SELECT_SHAPES])
+def test_selection_over_group_shapes(E, G, tg, k):
+    """Expert ids exact and weights within the routing gate against the
+    oracle, on every router path: logit waves then the selection launch (40
+    tokens), the one-kernel router (300), the logits GEMM (2100), and inside
+    moe_forward, where a few tokens select in the permute launch (5)."""
+    base = Workload(f"select-E{E}-G{G}", 2100, 128, E, G, tg, k, 64, 0, "bf16", "bf16",
+                    seed=40 + E + G, bias_boost=tuple(range(0, E, 7)), bias_boost_value=0.02)
+    inp = make_inputs(base, experts=False)
+    t = upload(inp, base)
+    cfg = binding.config_from(base)
+    ref_idx, ref_w, margin = oracle.route(base, inp["x"], inp["w_gate"], inp["e_bias"])
+    for T in (40, 300, 2100):
+        print(f"case E={E} G={G} tg={tg} k={k} T={T}", flush=True)
+        idx, w = binding.route(cfg, t["x"][:T].contiguous(), t["w_gate"], t["e_bias"])
+        torch.cuda.synchronize()
+        assert_routing_equal(idx, w, ref_idx[:T], ref_w[:T], margin[:T], f"route T={T}")
+    few = base.with_tokens(5)  # x of 5 tokens is the prefix of x of 2100
+    print(f"case E={E} G={G} tg={tg} k={k} forward T=5", flush=True)
+    inp5 = make_inputs(few)
+    layer = binding.MoELayer(few, inp5)
+    layer(binding.to_device(inp5["x"], "cuda", "x", few))
+    torch.cuda.synchronize()
+    assert_routing_equal(layer.topk_idx[:5], layer.topk_w[:5], ref_idx[:5], ref_w[:5], margin[:5],
+                         "forward T=5")
+
+
 def test_zero_tokens_and_growing_calls_reuse_one_workspace():
     wl = RAGGED_BF16
     inp = make_inputs(wl)
